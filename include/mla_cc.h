@@ -1,0 +1,281 @@
+/*
+ * mla_cc.h -- C ABI of libmla_cc.so: MLA chunked-context prefill on MI355X (gfx950).
+ *
+ * The method (vLLM PR #50613 digest, 实现拆解 items 1-3; PR #36540 and
+ * PR #49294 digests for the merge): the cached context of every prefill
+ * request is packed into chunks that fit a fixed workspace of rows; each chunk
+ * gathers its context K/V rows out of a paged cache, runs non-causal attention
+ * of its requests' new tokens against those rows (output + log-sum-exp), and
+ * LSE-merges the result into a per-token context partial.  The new tokens'
+ * causal self-attention (the suffix) is then merged with the partial.
+ *
+ * Conventions for every call:
+ *   - Return value: MLA_OK (0) or an MLA_ERR_* code; mla_status_string() gives
+ *     its text.  Arguments are checked before any HIP call, so argument errors
+ *     are reported without touching the GPU.  No C++ exception crosses the ABI.
+ *   - "dev" pointers are device pointers owned by the caller; "host" pointers
+ *     are host memory owned by the caller.  Device tensors must be 16-byte
+ *     aligned and contiguous in the layout stated.  The library keeps no
+ *     pointer after a call returns.
+ *   - Element types: bf16 tensors are passed as void* (2 bytes per element,
+ *     IEEE bfloat16 bits); LSE tensors are float (fp32) and head-major:
+ *     the LSE of head h, token t is at lse[h * lse_head_stride + t].
+ *   - Token-major layouts: q/k_new [T, H, 192], v_new and outputs [T, H, 128].
+ *     192 = 128 no-rope + 64 rope dims (MLA_QK_HEAD_DIM), 128 = MLA_V_HEAD_DIM.
+ *   - Paged cache: k_cache [num_blocks, block_size, H, 192],
+ *     v_cache [num_blocks, block_size, H, 128]; context position p of request
+ *     r is in block block_table[r * block_table_width + p / block_size], slot
+ *     p % block_size.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Device calls only
+ *     enqueue work on it; none synchronises or allocates device memory.
+ *   - An empty attention state is LSE = -inf with output 0.  Merges select
+ *     rather than multiply by zero, so the output of an empty side is never
+ *     read and may hold garbage or NaN.
+ */
+#ifndef MLA_CC_H
+#define MLA_CC_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+    MLA_OK = 0,
+    MLA_ERR_INVALID_ARG = 1, /* a null/misaligned pointer, a negative size, bad parameters */
+    MLA_ERR_CAPACITY = 2,    /* a caller-provided buffer is too small; the needed size is reported */
+    MLA_ERR_UNSUPPORTED = 3, /* a shape this build does not implement (e.g. other head dims) */
+    MLA_ERR_HIP = 4          /* a HIP runtime or launch error */
+};
+
+#define MLA_QK_HEAD_DIM 192
+#define MLA_V_HEAD_DIM 128
+#define MLA_ABI_VERSION 1
+
+/* Text of a status code (static storage). */
+const char* mla_status_string(int status);
+
+/* MLA_ABI_VERSION of the built library. */
+int mla_abi_version(void);
+
+/* One chunk of the plan.  Ranges are half-open.  token_begin/token_end index
+ * the batch's prefill tokens (query_start_loc of request_begin / request_end).
+ * Entries entry_begin .. entry_begin+num_entries-1 of the entry arrays describe
+ * requests request_begin.. in order: context offset (start) and row count. */
+typedef struct mla_chunk_desc {
+    int32_t request_begin, request_end;
+    int32_t token_begin, token_end;
+    int32_t entry_begin, num_entries;
+    int32_t num_rows;        /* workspace rows used: sum of the entries' row counts */
+    int32_t max_seq_len;     /* longest entry */
+    int32_t max_query_len;   /* longest query among the chunk's requests */
+    int32_t is_continuation; /* 1 if the first entry starts past context row 0 */
+} mla_chunk_desc;
+
+/*
+ * Pack every request's context rows into chunks of at most row_budget rows
+ * (plan_mla_context_chunks and aligned_split_len on the PR #50613 digest,
+ * 关键源码片段; invariants in 实现拆解 item 2).  Host only, pure, thread-safe,
+ * allocates nothing.
+ *
+ * Requests are visited in order; a request's remaining rows join the open chunk
+ * if they fit, otherwise the longest head of them that is a multiple of
+ * split_alignment, shorter than the remainder, at most max_context_chunk and
+ * fitting the free rows is placed and the chunk closes (it also closes when no
+ * such head exists).  Requests with context length 0 are in no chunk and close
+ * the open chunk.  Workspace rows equal context rows.
+ *
+ *   context_lens, query_lens  host int32[num_requests], >= 0
+ *   row_budget                workspace rows per chunk
+ *   max_context_chunk         cap on a split piece; <= 0 means row_budget
+ *   split_alignment           split granularity (normally the cache block size)
+ *   chunks / chunk_capacity   host output array; *num_chunks receives the count
+ *   entry_starts, entry_seq_lens / entry_capacity
+ *                             host output arrays; *num_entries receives the count
+ * Pass NULL output arrays (with capacity 0) to get only the counts.  If a
+ * capacity is too small the counts are still written and MLA_ERR_CAPACITY is
+ * returned.  MLA_ERR_INVALID_ARG if split_alignment < 1, row_budget <
+ * split_alignment, max_context_chunk < split_alignment, num_requests < 0, a
+ * length is negative, or the token/row totals overflow int32.
+ */
+int mla_plan_context_chunks(const int32_t* context_lens, const int32_t* query_lens, int32_t num_requests,
+                            int64_t row_budget, int64_t max_context_chunk, int32_t split_alignment,
+                            mla_chunk_desc* chunks, int32_t chunk_capacity, int32_t* num_chunks,
+                            int32_t* entry_starts, int32_t* entry_seq_lens, int32_t entry_capacity,
+                            int32_t* num_entries);
+
+/*
+ * Batch-wide token fields (PR #36540 digest, 实现拆解; PR #50613 digest,
+ * 实现拆解 item 1).  Host only.
+ *   *prefix_num_tokens  prefill_tokens_with_context: query_start_loc just past
+ *                       the last request with context (0 if none); tokens at or
+ *                       past it have no context.
+ *   empty_slices        host int32[2 * empty_capacity]: [begin, end) token range
+ *                       of each request with no context, in order; *num_empty
+ *                       receives the count (MLA_ERR_CAPACITY if it exceeds the
+ *                       capacity; NULL with capacity 0 to count only).
+ */
+int mla_prefill_token_info(const int32_t* context_lens, const int32_t* query_lens, int32_t num_requests,
+                           int64_t* prefix_num_tokens, int32_t* empty_slices, int32_t empty_capacity,
+                           int32_t* num_empty);
+
+/*
+ * init_mla_context_partial (PR #50613 digest, 实现拆解 item 3): set token rows
+ * [row_begin, row_end) of a context partial to the empty state: output 0 and
+ * LSE -inf.
+ *   out  dev bf16 [T, num_heads, head_dim] (pointer to token row 0)
+ *   lse  dev fp32, head-major with lse_head_stride >= row_end
+ * head_dim must be a positive multiple of 8.
+ */
+int mla_init_context_partial(void* out, float* lse, int64_t lse_head_stride, int64_t row_begin,
+                             int64_t row_end, int32_t num_heads, int32_t head_dim, void* stream);
+
+/*
+ * Gather one chunk's context rows out of the paged cache into the workspace
+ * (PR #50613 digest, 实现拆解 item 2: every context row is gathered exactly
+ * once).  Workspace row w belongs to the entry i with
+ * entry_row_offsets[i] <= w < entry_row_offsets[i+1]; it is context position
+ * p = entry_starts[i] + (w - entry_row_offsets[i]) of request entry_request[i]:
+ *   ws_k[w] = k_cache[block_table[req][p / block_size]][p % block_size]
+ * and likewise ws_v, all heads at once (a bit copy).
+ *   k_cache, v_cache     dev bf16 paged caches (layout above), num_blocks blocks
+ *   block_table          dev int32 [num_requests, block_table_width]
+ *   entry_request/starts dev int32 [num_entries]
+ *   entry_row_offsets    dev int32 [num_entries + 1], nondecreasing from 0 to num_rows
+ *   ws_k, ws_v           dev bf16 [>= num_rows, num_heads, 192 / 128]
+ * Exactly rows 0..num_rows-1 are written.  A row whose block index falls
+ * outside [0, num_blocks) or whose logical block is past block_table_width is
+ * filled with NaN instead of being read.
+ */
+int mla_gather_context(const void* k_cache, const void* v_cache, int64_t num_blocks, int32_t block_size,
+                       int32_t num_heads, const int32_t* block_table, int32_t block_table_width,
+                       const int32_t* entry_request, const int32_t* entry_starts,
+                       const int32_t* entry_row_offsets, int32_t num_entries, int32_t num_rows,
+                       void* ws_k, void* ws_v, void* stream);
+
+/*
+ * Varlen non-causal attention of one chunk (run_prefill_context_chunk on the
+ * PR #50613 digest, 实现拆解 item 4): for sequence i, queries
+ * cu_q[i]..cu_q[i+1]-1 attend to keys cu_k[i]..cu_k[i+1]-1:
+ *   s_j = scale * q . k_j,  out = sum_j softmax(s)_j v_j,  lse = ln sum_j e^{s_j}.
+ * bf16 MFMA products, fp32 accumulation, softmax and LSE.
+ *   q    dev bf16 [Tq, H, 192]    k dev bf16 [Tk, H, 192]    v dev bf16 [Tk, H, 128]
+ *   cu_q, cu_k  dev int32 [num_seqs + 1], nondecreasing from 0
+ *   max_q       >= every cu_q[i+1] - cu_q[i] (rows past it are not computed)
+ *   out  dev bf16 [Tq, H, 128]    lse dev fp32 [H, lse_head_stride >= Tq]
+ * A sequence with no keys gets (0, -inf).  Only rows of the listed sequences
+ * are written.
+ */
+int mla_context_chunk_attn(const void* q, const void* k, const void* v, const int32_t* cu_q,
+                           const int32_t* cu_k, int32_t num_seqs, int32_t max_q, int32_t num_heads,
+                           float scale, void* out, float* lse, int64_t lse_head_stride, void* stream);
+
+/*
+ * Causal self-attention of the new tokens (the suffix merged by
+ * merge_attn_states on the PR #36540 digest): token i of sequence s attends to
+ * tokens cu_q[s]..cu_q[s]+i (i.e. up to and including itself).
+ * Layouts as mla_context_chunk_attn with k = k_new, v = v_new sharing cu_q.
+ */
+int mla_causal_suffix_attn(const void* q, const void* k_new, const void* v_new, const int32_t* cu_q,
+                           int32_t num_seqs, int32_t max_q, int32_t num_heads, float scale, void* out,
+                           float* lse, int64_t lse_head_stride, void* stream);
+
+/*
+ * merge_attn_states with prefill_tokens_with_context (PR #36540 digest,
+ * 实现拆解, CUDA kernel layer; empty states per the PR #49294 digest):
+ * for token t < prefix_num_tokens and each head:
+ *   both LSEs -inf  -> output 0, LSE -inf (never NaN)
+ *   prefix -inf     -> the suffix row (bit copy) and LSE
+ *   suffix -inf     -> the prefix row (bit copy) and LSE
+ *   otherwise       -> LSE-weighted average, LSE = ln(e^Lp + e^Ls)
+ * for t >= prefix_num_tokens: the suffix row and LSE (prefix not read).
+ *   out, prefix_out, suffix_out  dev bf16 [T, H, head_dim]; head_dim a multiple of 8
+ *   out_lse (may be NULL), prefix_lse, suffix_lse  dev fp32 head-major with their strides
+ * out may be the same pointer as prefix_out (and out_lse as prefix_lse): this
+ * is accumulate_mla_context_chunk (PR #50613 digest, 实现拆解 item 3).  Other
+ * overlaps are not allowed.
+ */
+int mla_merge_attn_states(void* out, float* out_lse, const void* prefix_out, const float* prefix_lse,
+                          const void* suffix_out, const float* suffix_lse, int64_t num_tokens,
+                          int32_t num_heads, int32_t head_dim, int64_t out_lse_stride,
+                          int64_t prefix_lse_stride, int64_t suffix_lse_stride,
+                          int64_t prefix_num_tokens, void* stream);
+
+/* Inputs, outputs and scratch of one chunked prefill (all dev pointers are
+ * caller-owned; lens are host arrays). */
+typedef struct mla_chunked_prefill_params {
+    const void* q;              /* dev bf16 [T, H, 192] */
+    const void* k_new;          /* dev bf16 [T, H, 192] */
+    const void* v_new;          /* dev bf16 [T, H, 128] */
+    const void* k_cache;        /* dev bf16 [num_blocks, block_size, H, 192] */
+    const void* v_cache;        /* dev bf16 [num_blocks, block_size, H, 128] */
+    const int32_t* block_table; /* dev int32 [num_requests, block_table_width] */
+    int64_t num_blocks;
+    int32_t block_size;
+    int32_t block_table_width;
+    const int32_t* context_lens; /* host int32 [num_requests] */
+    const int32_t* query_lens;   /* host int32 [num_requests] */
+    int32_t num_requests;
+    int32_t num_heads;
+    float scale;
+    int64_t workspace_rows;    /* row_budget of the planner */
+    int64_t max_context_chunk; /* <= 0: workspace_rows */
+    int32_t split_alignment;
+    void* out;      /* dev bf16 [T, H, 128] */
+    float* out_lse; /* dev fp32 [H, T] or NULL */
+    void* scratch;  /* dev, >= mla_chunked_prefill_scratch_size bytes, 256-byte aligned */
+    int64_t scratch_bytes;
+} mla_chunked_prefill_params;
+
+/* Scratch bytes mla_chunked_prefill needs for these params (host only;
+ * pointer fields are not read). */
+int mla_chunked_prefill_scratch_size(const mla_chunked_prefill_params* params, int64_t* bytes);
+
+/*
+ * The whole chunked-context prefill (the _compute_prefill_context loop on the
+ * PR #50613 digest, 实现拆解 item 3, followed by the final merge of the
+ * PR #36540 digest): plan on the host, upload the chunk metadata once, then
+ * per chunk gather -> chunk attention -> accumulate into the context partial,
+ * then the causal suffix attention and merge_attn_states with
+ * prefix_num_tokens.  Rows of requests without context get their context
+ * partial initialised to (0, -inf); a chunk's rows that no earlier chunk wrote
+ * are written directly (so a single chunk covering every token needs no
+ * partial initialisation or merge).  Enqueues on `stream`; the host returns
+ * once the work is enqueued.  Successive calls may overlap: the metadata is
+ * staged through pinned host buffers that are recycled only after their copy
+ * has completed.
+ */
+int mla_chunked_prefill(const mla_chunked_prefill_params* params, void* stream);
+
+/*
+ * Kernel timing, a measurement aid (not part of the method).  While enabled,
+ * every kernel the library launches is bracketed by a pair of HIP events
+ * recorded on the launch's own stream.  mla_kernel_timing_read waits for the
+ * recorded events, adds each kernel's elapsed time into times[kind] (an array
+ * of MLA_KERNEL_KINDS entries, launches and total milliseconds per kind),
+ * and forgets them.  Enabling costs two event records per launch; disabling
+ * drops any unread events.  Thread-safe; events are per process.
+ */
+enum {
+    MLA_KERNEL_INIT = 0,
+    MLA_KERNEL_GATHER = 1,
+    MLA_KERNEL_CHUNK_ATTN = 2,
+    MLA_KERNEL_SUFFIX_ATTN = 3,
+    MLA_KERNEL_MERGE = 4,
+    MLA_KERNEL_KINDS = 5
+};
+
+typedef struct mla_kernel_time {
+    int64_t launches;
+    double total_ms;
+} mla_kernel_time;
+
+int mla_kernel_timing_enable(int enable);
+int mla_kernel_timing_read(mla_kernel_time* times);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_CC_H */

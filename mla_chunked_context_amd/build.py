@@ -1,0 +1,67 @@
+"""Build libmla_cc.so in-tree with hipcc for gfx950.
+
+Every source is compiled on each call (``build()`` is the does-it-build check);
+objects go to ``_build/`` next to this file and the library to
+``mla_chunked_context_amd/libmla_cc.so``.
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+from concurrent.futures import ThreadPoolExecutor
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+BUILD_DIR = os.path.join(PKG, "_build")
+LIB_PATH = os.path.join(PKG, "libmla_cc.so")
+
+SOURCES = ["planner.cpp", "memory_ops.hip", "attention.hip", "pipeline.hip", "timing.hip"]
+
+ARCH = "gfx950"
+# no packed-fp32 instructions in device code
+DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function", f"-I{INCLUDE}", f"-I{CSRC}"]
+
+
+def _hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found (ROCm is required to build libmla_cc.so)")
+
+
+def _compile(src: str, hipcc: str, extra) -> str:
+    path = os.path.join(CSRC, src)
+    obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
+    if src.endswith(".hip"):
+        cmd = [hipcc, "-x", "hip", f"--offload-arch={ARCH}", *DEVICE_FLAGS, *COMMON, *extra, "-c", path, "-o", obj]
+    else:
+        cmd = [hipcc, "-x", "c++", *COMMON, *extra, "-c", path, "-o", obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    return obj
+
+
+def build(verbose: bool = False, extra_flags=()) -> str:
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    hipcc = _hipcc()
+    with ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
+        objs = list(ex.map(lambda s: _compile(s, hipcc, list(extra_flags)), SOURCES))
+    tmp = LIB_PATH + ".tmp"
+    cmd = [hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, LIB_PATH)
+    if verbose:
+        print(f"built {LIB_PATH}", file=sys.stderr)
+    return LIB_PATH
+
+
+if __name__ == "__main__":
+    build(verbose=True)

@@ -1,0 +1,379 @@
+// Varlen attention with LSE for MLA prefill on gfx950 (qk dim 192, v dim 128).
+//
+// One kernel serves both attention steps of the chunked prefill:
+//   * chunk attention (non-causal): the prefill queries of each request in a
+//     chunk against that request's gathered context rows
+//     (run_prefill_context_chunk, vLLM PR #50613 digest, 实现拆解 item 4);
+//   * suffix attention (causal): new tokens against the new tokens up to
+//     themselves (the suffix merged by merge_attn_states, PR #36540 digest).
+// Output: O = softmax(scale * q k^T) v in bf16 and LSE = ln sum exp(scale q.k)
+// in fp32, stored head-major.
+//
+// Work decomposition
+//   A workgroup owns 128 queries of one (sequence, head): 4 waves x 32 queries.
+//   Keys stream through LDS in tiles of 64 (K row-major, V transposed), shared
+//   by the 4 waves; the next tile's global loads are in flight while the
+//   current tile is computed.  Workgroup ids are remapped so that the query
+//   tiles of one (sequence, head) run on the same XCD and share its L2.
+//
+// MFMA formulation (v_mfma_f32_32x32x16_bf16, wave64)
+//   S^T = K Q^T : A = K tile rows from LDS, B = Q fragments held in registers.
+//     The accumulator gives each lane one query column (lane & 31) and 16 of
+//     each 32-key block's rows, so the running max / sum of a query live in
+//     one lane pair (lane, lane ^ 32): no cross-lane reductions except one
+//     swap per tile for the max.
+//   O^T = V^T P^T : B = P^T taken directly from the S^T accumulators
+//     (converted to bf16); A = V^T from LDS.  The 8 keys a lane contributes
+//     to one 16-key step are not contiguous in key order (accumulator rows
+//     g*4+{0..3} and 8+g*4+{0..3}); V^T is stored in LDS with bits 2 and 3 of
+//     the key index swapped so that those 8 keys are one 16-byte read.
+//   Both operands of an MFMA use the same (lane group, slot) -> k mapping, so
+//   the products are correct whatever order the hardware assigns to k.
+//
+// Softmax: base-2 exponentials with the scale folded in, p = 2^(s*c - m),
+// c = scale * log2(e); the LSE is converted back to natural log at the end.
+#include <cmath>
+
+#include "device.h"
+
+namespace mla {
+
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kThreads = 256;
+constexpr int kWaves = 4;
+constexpr int kQPerWave = 32;
+constexpr int kBlockM = kWaves * kQPerWave;  // queries per workgroup
+constexpr int kBlockN = 64;                  // keys per tile
+constexpr int kKStride = kDk + 8;            // K tile LDS row stride (elements): 400 B
+constexpr int kVtStride = kBlockN + 8;       // V^T tile LDS row stride (elements): 144 B
+constexpr int kKVecPerRow = kDk / 8;         // 24 16-byte vectors per K row
+constexpr int kKLoads = kBlockN * kKVecPerRow / kThreads;  // 6 per thread
+constexpr int kVLoads = 4;                                  // 4 keys x 8 dims per thread
+
+struct AttnArgs {
+    const bf16_t* q;
+    const bf16_t* k;
+    const bf16_t* v;
+    const int32_t* cu_q;
+    const int32_t* cu_k;
+    bf16_t* out;
+    float* lse;
+    int64_t lse_stride;
+    int32_t num_seqs;
+    int32_t q_tiles;
+    int32_t heads;
+    int32_t total_tiles;
+    float scale_log2;  // scale * log2(e)
+};
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    bf16x2_t v = {static_cast<__bf16>(lo), static_cast<__bf16>(hi)};
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+// Position of key (0..63) inside a V^T LDS row: bits 2 and 3 swapped.
+__device__ __forceinline__ int vt_pos(int key) {
+    return (key & ~12) | ((key & 4) << 1) | ((key & 8) >> 1);
+}
+
+// Workgroups are dealt to the 8 XCDs round-robin; map them so that each XCD
+// processes a contiguous range of logical tiles.
+__device__ __forceinline__ int32_t xcd_logical_tile(int32_t bid, int32_t total) {
+    const int32_t per = total / kNumXcd;
+    if (bid >= per * kNumXcd) return bid;
+    return (bid % kNumXcd) * per + bid / kNumXcd;
+}
+
+template <bool kCausal>
+__global__ __launch_bounds__(kThreads, 2) void attention_kernel(AttnArgs a) {
+    __shared__ __attribute__((aligned(16))) bf16_t k_lds[kBlockN * kKStride];
+    __shared__ __attribute__((aligned(16))) bf16_t vt_lds[kDv * kVtStride];
+
+    const int32_t tile = xcd_logical_tile(blockIdx.x, a.total_tiles);
+    int32_t qt = tile % a.q_tiles;
+    const int32_t rest = tile / a.q_tiles;
+    const int32_t head = rest % a.heads;
+    const int32_t seq = rest / a.heads;
+    if (kCausal) qt = a.q_tiles - 1 - qt;  // longest causal tiles first
+
+    const int32_t q_begin = a.cu_q[seq];
+    const int32_t q_len = a.cu_q[seq + 1] - q_begin;
+    if (qt * kBlockM >= q_len) return;
+    const int32_t k_begin = kCausal ? q_begin : a.cu_k[seq];
+    const int32_t k_len = kCausal ? q_len : a.cu_k[seq + 1] - k_begin;
+    const int32_t kv_end = kCausal ? min(k_len, (qt + 1) * kBlockM) : k_len;
+
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6;
+    const int lane = tid & 63;
+    const int l32 = lane & 31;
+    const int g = lane >> 5;
+    const int H = a.heads;
+
+    // ---- Q fragments (B operand of S^T = K Q^T), kept in registers
+    const int32_t q_row = qt * kBlockM + wave * kQPerWave + l32;  // row inside the sequence
+    const bool q_valid = q_row < q_len;
+    bf16x8 qf[kDk / 16];
+    {
+        const uint4* qp = reinterpret_cast<const uint4*>(
+            a.q + (static_cast<int64_t>(q_begin + (q_valid ? q_row : 0)) * H + head) * kDk + g * 8);
+#pragma unroll
+        for (int ks = 0; ks < kDk / 16; ++ks) {
+            uint4 x = q_valid ? qp[ks * 2] : make_uint4(0u, 0u, 0u, 0u);
+            qf[ks] = __builtin_bit_cast(bf16x8, x);
+        }
+    }
+
+    f32x16 o_acc[kDv / 32];
+#pragma unroll
+    for (int db = 0; db < kDv / 32; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o_acc[db][r] = 0.f;
+    float m_run = -INFINITY;  // running max of s * c over this lane pair's query
+    float l_run = 0.f;        // this lane's share of the running sum
+
+    // ---- staging of one key tile: global -> registers -> LDS
+    uint4 kreg[kKLoads];
+    uint4 vreg[kVLoads];
+    const int vkq = tid & 15;  // keys 4*vkq .. 4*vkq+3 of the tile
+    const int vdc = tid >> 4;  // dims 8*vdc .. 8*vdc+7
+
+    auto load_tile = [&](int32_t k0) {
+#pragma unroll
+        for (int i = 0; i < kKLoads; ++i) {
+            const int vidx = tid + i * kThreads;
+            const int key = vidx / kKVecPerRow;
+            const int c = vidx - key * kKVecPerRow;
+            const int32_t kr = k0 + key;
+            kreg[i] = kr < kv_end ? *reinterpret_cast<const uint4*>(
+                                        a.k + (static_cast<int64_t>(k_begin + kr) * H + head) * kDk + c * 8)
+                                  : make_uint4(0u, 0u, 0u, 0u);
+        }
+#pragma unroll
+        for (int u = 0; u < kVLoads; ++u) {
+            const int32_t kr = k0 + vkq * 4 + u;
+            vreg[u] = kr < kv_end ? *reinterpret_cast<const uint4*>(
+                                        a.v + (static_cast<int64_t>(k_begin + kr) * H + head) * kDv + vdc * 8)
+                                  : make_uint4(0u, 0u, 0u, 0u);
+        }
+    };
+    auto store_tile = [&]() {
+#pragma unroll
+        for (int i = 0; i < kKLoads; ++i) {
+            const int vidx = tid + i * kThreads;
+            const int key = vidx / kKVecPerRow;
+            const int c = vidx - key * kKVecPerRow;
+            *reinterpret_cast<uint4*>(&k_lds[key * kKStride + c * 8]) = kreg[i];
+        }
+        // transpose 4 keys x 8 dims into 8 rows (dims) of 4 keys
+        const int pos = vt_pos(vkq * 4);
+        const uint32_t w[4][4] = {{vreg[0].x, vreg[0].y, vreg[0].z, vreg[0].w},
+                                  {vreg[1].x, vreg[1].y, vreg[1].z, vreg[1].w},
+                                  {vreg[2].x, vreg[2].y, vreg[2].z, vreg[2].w},
+                                  {vreg[3].x, vreg[3].y, vreg[3].z, vreg[3].w}};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t lo_e0 = (w[0][i] & 0xffffu) | (w[1][i] << 16);
+            const uint32_t hi_e0 = (w[2][i] & 0xffffu) | (w[3][i] << 16);
+            const uint32_t lo_e1 = (w[0][i] >> 16) | (w[1][i] & 0xffff0000u);
+            const uint32_t hi_e1 = (w[2][i] >> 16) | (w[3][i] & 0xffff0000u);
+            const int d0 = vdc * 8 + 2 * i;
+            *reinterpret_cast<uint2*>(&vt_lds[d0 * kVtStride + pos]) = make_uint2(lo_e0, hi_e0);
+            *reinterpret_cast<uint2*>(&vt_lds[(d0 + 1) * kVtStride + pos]) = make_uint2(lo_e1, hi_e1);
+        }
+    };
+
+    const int32_t n_tiles = (kv_end + kBlockN - 1) / kBlockN;
+    if (n_tiles > 0) {
+        load_tile(0);
+        store_tile();
+    }
+    __syncthreads();
+
+    for (int32_t t = 0; t < n_tiles; ++t) {
+        const int32_t k0 = t * kBlockN;
+        if (t + 1 < n_tiles) load_tile(k0 + kBlockN);
+
+        // ---- S^T = K Q^T for two 32-key blocks
+        f32x16 s[2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
+            const bf16_t* krow = &k_lds[(kb * 32 + l32) * kKStride + g * 8];
+#pragma unroll
+            for (int ks = 0; ks < kDk / 16; ++ks) {
+                const bf16x8 af = *reinterpret_cast<const bf16x8*>(krow + ks * 16);
+                s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, qf[ks], s[kb], 0, 0, 0);
+            }
+        }
+
+        // ---- mask keys past the end (and above the diagonal when causal)
+        const bool need_mask = (k0 + kBlockN > kv_end) ||
+                               (kCausal && k0 + kBlockN - 1 > qt * kBlockM + wave * kQPerWave);
+        if (need_mask) {
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int32_t key = k0 + kb * 32 + (r >> 2) * 8 + g * 4 + (r & 3);
+                    const bool dead = key >= kv_end || (kCausal && key > q_row);
+                    if (dead) s[kb][r] = -INFINITY;
+                }
+        }
+
+        // ---- online softmax (base 2), one query per lane pair
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float m_new = fmaxf(m_run, mx * a.scale_log2);
+        const float m_use = m_new == -INFINITY ? 0.f : m_new;
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+        m_run = m_new;
+        float psum = 0.f;
+        bf16x8 pb[2][2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+                uint32_t pk[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const float p0 = __builtin_amdgcn_exp2f(fmaf(s[kb][hh * 8 + 2 * j], a.scale_log2, -m_use));
+                    const float p1 = __builtin_amdgcn_exp2f(fmaf(s[kb][hh * 8 + 2 * j + 1], a.scale_log2, -m_use));
+                    psum += p0 + p1;
+                    pk[j] = pack_bf16x2(p0, p1);
+                }
+                pb[kb][hh] = __builtin_bit_cast(bf16x8, make_uint4(pk[0], pk[1], pk[2], pk[3]));
+            }
+        l_run = l_run * alpha + psum;
+#pragma unroll
+        for (int db = 0; db < kDv / 32; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) o_acc[db][r] *= alpha;
+
+        // ---- O^T += V^T P^T
+#pragma unroll
+        for (int db = 0; db < kDv / 32; ++db) {
+            const bf16_t* vrow = &vt_lds[(db * 32 + l32) * kVtStride + g * 8];
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh) {
+                    const bf16x8 af = *reinterpret_cast<const bf16x8*>(vrow + kb * 32 + hh * 16);
+                    o_acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, pb[kb][hh], o_acc[db], 0, 0, 0);
+                }
+        }
+
+        __syncthreads();
+        if (t + 1 < n_tiles) store_tile();
+        __syncthreads();
+    }
+
+    // ---- epilogue: normalise, write bf16 output rows and the LSE
+    const float l_tot = l_run + __shfl_xor(l_run, 32);
+    if (!q_valid) return;
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    bf16_t* orow = a.out + (static_cast<int64_t>(q_begin + q_row) * H + head) * kDv + g * 4;
+#pragma unroll
+    for (int db = 0; db < kDv / 32; ++db)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+            const uint32_t lo = pack_bf16x2(o_acc[db][r4 * 4 + 0] * inv, o_acc[db][r4 * 4 + 1] * inv);
+            const uint32_t hi = pack_bf16x2(o_acc[db][r4 * 4 + 2] * inv, o_acc[db][r4 * 4 + 3] * inv);
+            *reinterpret_cast<uint2*>(orow + db * 32 + r4 * 8) = make_uint2(lo, hi);
+        }
+    if (g == 0) {
+        const float lse = l_tot > 0.f ? (m_run + log2f(l_tot)) * 0.69314718055994531f : -INFINITY;
+        a.lse[head * a.lse_stride + q_begin + q_row] = lse;
+    }
+}
+
+}  // namespace
+
+int launch_attention(const bf16_t* q, const bf16_t* k, const bf16_t* v, const int32_t* cu_q, const int32_t* cu_k,
+                     int32_t num_seqs, int32_t max_q, int32_t heads, float scale, bool causal, bf16_t* out,
+                     float* lse, int64_t lse_stride, hipStream_t stream) {
+    if (num_seqs <= 0 || max_q <= 0) return MLA_OK;
+    AttnArgs a{};
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.cu_q = cu_q;
+    a.cu_k = causal ? cu_q : cu_k;
+    a.out = out;
+    a.lse = lse;
+    a.lse_stride = lse_stride;
+    a.num_seqs = num_seqs;
+    a.q_tiles = (max_q + kBlockM - 1) / kBlockM;
+    a.heads = heads;
+    const int64_t total = static_cast<int64_t>(num_seqs) * a.q_tiles * heads;
+    if (total > INT32_MAX) return MLA_ERR_UNSUPPORTED;
+    a.total_tiles = static_cast<int32_t>(total);
+    a.scale_log2 = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
+    TimedLaunch timed(causal ? MLA_KERNEL_SUFFIX_ATTN : MLA_KERNEL_CHUNK_ATTN, stream);
+    if (causal)
+        hipLaunchKernelGGL(attention_kernel<true>, dim3(a.total_tiles), dim3(kThreads), 0, stream, a);
+    else
+        hipLaunchKernelGGL(attention_kernel<false>, dim3(a.total_tiles), dim3(kThreads), 0, stream, a);
+    return hip_status(hipGetLastError());
+}
+
+}  // namespace mla
+
+// ----------------------------------------------------------------------------
+// C ABI
+
+namespace {
+
+int check_attention_args(const void* q, const void* k, const void* v, const int32_t* cu_q, int32_t num_seqs,
+                         int32_t max_q, int32_t num_heads, float scale, const void* out, const float* lse,
+                         int64_t lse_head_stride) {
+    if (num_seqs < 0 || max_q < 0 || num_heads < 1) return MLA_ERR_INVALID_ARG;
+    if (!(scale > 0.f) || !std::isfinite(scale)) return MLA_ERR_INVALID_ARG;
+    if (num_seqs == 0 || max_q == 0) return MLA_OK;
+    if (q == nullptr || k == nullptr || v == nullptr || cu_q == nullptr || out == nullptr || lse == nullptr)
+        return MLA_ERR_INVALID_ARG;
+    if (!mla::aligned16(q) || !mla::aligned16(k) || !mla::aligned16(v) || !mla::aligned16(out))
+        return MLA_ERR_INVALID_ARG;
+    if (lse_head_stride < 1) return MLA_ERR_INVALID_ARG;
+    return MLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int mla_context_chunk_attn(const void* q, const void* k, const void* v, const int32_t* cu_q, const int32_t* cu_k,
+                           int32_t num_seqs, int32_t max_q, int32_t num_heads, float scale, void* out, float* lse,
+                           int64_t lse_head_stride, void* stream) {
+    int st = check_attention_args(q, k, v, cu_q, num_seqs, max_q, num_heads, scale, out, lse, lse_head_stride);
+    if (st != MLA_OK || num_seqs == 0 || max_q == 0) return st;
+    if (cu_k == nullptr) return MLA_ERR_INVALID_ARG;
+    return mla::launch_attention(static_cast<const mla::bf16_t*>(q), static_cast<const mla::bf16_t*>(k),
+                                 static_cast<const mla::bf16_t*>(v), cu_q, cu_k, num_seqs, max_q, num_heads, scale,
+                                 false, static_cast<mla::bf16_t*>(out), lse, lse_head_stride,
+                                 static_cast<hipStream_t>(stream));
+}
+
+int mla_causal_suffix_attn(const void* q, const void* k_new, const void* v_new, const int32_t* cu_q,
+                           int32_t num_seqs, int32_t max_q, int32_t num_heads, float scale, void* out, float* lse,
+                           int64_t lse_head_stride, void* stream) {
+    int st = check_attention_args(q, k_new, v_new, cu_q, num_seqs, max_q, num_heads, scale, out, lse,
+                                  lse_head_stride);
+    if (st != MLA_OK || num_seqs == 0 || max_q == 0) return st;
+    return mla::launch_attention(static_cast<const mla::bf16_t*>(q), static_cast<const mla::bf16_t*>(k_new),
+                                 static_cast<const mla::bf16_t*>(v_new), cu_q, cu_q, num_seqs, max_q, num_heads,
+                                 scale, true, static_cast<mla::bf16_t*>(out), lse, lse_head_stride,
+                                 static_cast<hipStream_t>(stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,60 @@
+// Internal declarations shared by the HIP translation units of libmla_cc.so.
+// gfx950 only: MFMA builtins and the bf16 conversion instructions of CDNA4
+// are used directly.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "mla_cc.h"
+
+namespace mla {
+
+using bf16_t = uint16_t;  // storage type of bfloat16 tensors (raw bits)
+
+constexpr int kDk = MLA_QK_HEAD_DIM;  // 192
+constexpr int kDv = MLA_V_HEAD_DIM;   // 128
+constexpr int kNumXcd = 8;            // MI355X: 8 XCDs, workgroups dealt round-robin
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+inline int hip_status(hipError_t e) { return e == hipSuccess ? MLA_OK : MLA_ERR_HIP; }
+
+// Optional event bracketing of launches (mla_kernel_timing_enable).  A
+// TimedLaunch records a start event at construction and an end event at
+// destruction when timing is on; it does nothing otherwise.
+class TimedLaunch {
+  public:
+    TimedLaunch(int kind, hipStream_t stream);
+    ~TimedLaunch();
+    TimedLaunch(const TimedLaunch&) = delete;
+    TimedLaunch& operator=(const TimedLaunch&) = delete;
+
+  private:
+    int kind_;
+    hipStream_t stream_;
+    hipEvent_t start_ = nullptr;
+};
+
+// Launchers used by both the C ABI wrappers (after argument checks) and the
+// chunked-prefill driver.  They only enqueue work and report launch errors.
+int launch_init_partial(bf16_t* out, float* lse, int64_t lse_stride, int64_t row_begin, int64_t row_end,
+                        int32_t heads, int32_t head_dim, hipStream_t stream);
+
+int launch_merge(bf16_t* out, float* out_lse, const bf16_t* p_out, const float* p_lse, const bf16_t* s_out,
+                 const float* s_lse, int64_t tokens, int32_t heads, int32_t head_dim, int64_t out_stride,
+                 int64_t p_stride, int64_t s_stride, int64_t prefix_num_tokens, hipStream_t stream);
+
+int launch_gather(const bf16_t* k_cache, const bf16_t* v_cache, int64_t num_blocks, int32_t block_size,
+                  int32_t heads, const int32_t* block_table, int32_t bt_width, const int32_t* e_req,
+                  const int32_t* e_start, const int32_t* e_off, int32_t n_entries, int32_t num_rows,
+                  bf16_t* ws_k, bf16_t* ws_v, hipStream_t stream);
+
+// Varlen attention.  causal: query i of a sequence sees keys 0..i of the same
+// sequence (cu_k must then equal cu_q).
+int launch_attention(const bf16_t* q, const bf16_t* k, const bf16_t* v, const int32_t* cu_q,
+                     const int32_t* cu_k, int32_t num_seqs, int32_t max_q, int32_t heads, float scale,
+                     bool causal, bf16_t* out, float* lse, int64_t lse_stride, hipStream_t stream);
+
+}  // namespace mla

@@ -1,0 +1,305 @@
+// Bandwidth-bound kernels of MLA chunked-context prefill on gfx950:
+//   * init of the context partial (output 0, LSE -inf),
+//   * merge_attn_states (LSE-weighted merge, threshold copy, empty-state select),
+//   * gather of a chunk's context rows out of the paged KV cache.
+// All move 16-byte vectors; consecutive lanes touch consecutive vectors.
+#include <cmath>
+
+#include "device.h"
+
+namespace mla {
+
+namespace {
+
+constexpr int kThreads = 256;
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
+
+// fp32 -> bf16 with round-to-nearest-even (v_cvt_pk_bf16_f32 on gfx950)
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    bf16x2_t v = {static_cast<__bf16>(lo), static_cast<__bf16>(hi)};
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+// ---------------------------------------------------------------- init
+
+__global__ __launch_bounds__(kThreads) void init_partial_kernel(uint4* out, float* lse, int64_t lse_stride,
+                                                                int64_t row_begin, int64_t rows, int32_t heads,
+                                                                int64_t vec_per_token) {
+    const int64_t nvec = rows * vec_per_token;
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * kThreads;
+    const int64_t gid = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
+    for (int64_t i = gid; i < nvec; i += stride) out[i] = make_uint4(0u, 0u, 0u, 0u);
+    const int64_t nl = rows * heads;
+    for (int64_t i = gid; i < nl; i += stride) {
+        const int64_t h = i / rows;
+        lse[h * lse_stride + row_begin + (i - h * rows)] = -INFINITY;
+    }
+}
+
+// ---------------------------------------------------------------- merge
+
+struct MergeArgs {
+    uint4* out;
+    float* out_lse;
+    const uint4* p_out;
+    const float* p_lse;
+    const uint4* s_out;
+    const float* s_lse;
+    int64_t tokens;
+    int32_t heads;
+    int32_t vec_per_row;  // head_dim / 8
+    int64_t out_stride, p_stride, s_stride;
+    int64_t prefix_num_tokens;
+};
+
+// Merge of one 8-element vector of one (token, head) row.  The prefix side is
+// not read at or past the threshold, and the side of an empty state (LSE -inf)
+// is never read: the result is selected, not multiplied by zero.
+__device__ __forceinline__ void merge_vec(const MergeArgs& a, int64_t t, int32_t h, int64_t vec_index,
+                                          bool write_lse) {
+    const float sl = a.s_lse[h * a.s_stride + t];
+    float ol;
+    uint4 res;
+    if (t >= a.prefix_num_tokens) {
+        res = a.s_out[vec_index];
+        ol = sl;
+    } else {
+        const float pl = a.p_lse[h * a.p_stride + t];
+        const bool pe = pl == -INFINITY, se = sl == -INFINITY;
+        if (pe && se) {
+            res = make_uint4(0u, 0u, 0u, 0u);
+            ol = -INFINITY;
+        } else if (pe) {
+            res = a.s_out[vec_index];
+            ol = sl;
+        } else if (se) {
+            res = a.p_out[vec_index];
+            ol = pl;
+        } else {
+            const float m = fmaxf(pl, sl);
+            const float wp = expf(pl - m), ws = expf(sl - m);
+            const float tot = wp + ws;
+            const float fp = wp / tot, fs = ws / tot;
+            const uint4 pv = a.p_out[vec_index], sv = a.s_out[vec_index];
+            const uint32_t pw[4] = {pv.x, pv.y, pv.z, pv.w};
+            const uint32_t sw[4] = {sv.x, sv.y, sv.z, sv.w};
+            uint32_t rw[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const float lo = fp * bf16_to_f32(pw[k] & 0xffffu) + fs * bf16_to_f32(sw[k] & 0xffffu);
+                const float hi = fp * bf16_to_f32(pw[k] >> 16) + fs * bf16_to_f32(sw[k] >> 16);
+                rw[k] = pack_bf16x2(lo, hi);
+            }
+            res = make_uint4(rw[0], rw[1], rw[2], rw[3]);
+            ol = m + logf(tot);
+        }
+    }
+    a.out[vec_index] = res;
+    if (write_lse && a.out_lse != nullptr) a.out_lse[h * a.out_stride + t] = ol;
+}
+
+// head_dim 128: a block covers 16 consecutive tokens x 4 heads; 16 lanes per
+// (token, head) row of 256 bytes.  Consecutive tokens of one head share the
+// LSE cache lines.
+constexpr int kMergeTokens = 16;
+constexpr int kMergeHeads = 4;
+
+__global__ __launch_bounds__(kThreads) void merge_kernel_d128(MergeArgs a) {
+    const int lane_vec = threadIdx.x & 15;
+    const int64_t t = static_cast<int64_t>(blockIdx.x) * kMergeTokens + (threadIdx.x >> 4);
+    if (t >= a.tokens) return;
+    const int32_t h0 = blockIdx.y * kMergeHeads;
+#pragma unroll
+    for (int hh = 0; hh < kMergeHeads; ++hh) {
+        const int32_t h = h0 + hh;
+        if (h >= a.heads) break;
+        merge_vec(a, t, h, (t * a.heads + h) * 16 + lane_vec, lane_vec == 0);
+    }
+}
+
+// any head_dim that is a multiple of 8
+__global__ __launch_bounds__(kThreads) void merge_kernel_generic(MergeArgs a) {
+    const int64_t total = a.tokens * a.heads * a.vec_per_row;
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * kThreads;
+    for (int64_t i = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x; i < total; i += stride) {
+        const int64_t row = i / a.vec_per_row;
+        const int32_t j = static_cast<int32_t>(i - row * a.vec_per_row);
+        const int64_t t = row / a.heads;
+        const int32_t h = static_cast<int32_t>(row - t * a.heads);
+        merge_vec(a, t, h, i, j == 0);
+    }
+}
+
+// ---------------------------------------------------------------- gather
+
+constexpr int kGatherRows = 4;    // workspace rows per block
+constexpr int kGatherUnroll = 4;  // 16-byte vectors in flight per lane per pass
+
+__device__ __forceinline__ void copy_row(const uint4* __restrict__ src, uint4* __restrict__ dst, int n,
+                                         bool ok) {
+    const uint4 nan4 = make_uint4(0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u);
+    for (int base = threadIdx.x; base < n; base += kThreads * kGatherUnroll) {
+        uint4 r[kGatherUnroll];
+#pragma unroll
+        for (int u = 0; u < kGatherUnroll; ++u) {
+            const int v = base + u * kThreads;
+            r[u] = (ok && v < n) ? src[v] : nan4;
+        }
+#pragma unroll
+        for (int u = 0; u < kGatherUnroll; ++u) {
+            const int v = base + u * kThreads;
+            if (v < n) dst[v] = r[u];
+        }
+    }
+}
+
+__global__ __launch_bounds__(kThreads) void gather_kernel(
+    const uint4* __restrict__ k_cache, const uint4* __restrict__ v_cache, int64_t num_blocks, int32_t block_size,
+    int32_t heads, const int32_t* __restrict__ block_table, int32_t bt_width, const int32_t* __restrict__ e_req,
+    const int32_t* __restrict__ e_start, const int32_t* __restrict__ e_off, int32_t n_entries, int32_t num_rows,
+    uint4* __restrict__ ws_k, uint4* __restrict__ ws_v) {
+    const int32_t row0 = blockIdx.x * kGatherRows;
+    if (row0 >= num_rows) return;
+    // entry owning row0: the last i with e_off[i] <= row0 (skips empty entries)
+    int32_t lo = 0, hi = n_entries - 1;
+    while (lo < hi) {
+        const int32_t mid = (lo + hi + 1) >> 1;
+        if (e_off[mid] <= row0) lo = mid; else hi = mid - 1;
+    }
+    int32_t e = lo;
+    const int kvec = heads * (kDk / 8), vvec = heads * (kDv / 8);
+    for (int rr = 0; rr < kGatherRows; ++rr) {
+        const int32_t w = row0 + rr;
+        if (w >= num_rows) break;
+        while (e + 1 < n_entries && e_off[e + 1] <= w) ++e;
+        const int32_t req = e_req[e];
+        const int64_t p = static_cast<int64_t>(e_start[e]) + (w - e_off[e]);
+        const int64_t lb = p / block_size;
+        const int32_t slot = static_cast<int32_t>(p - lb * block_size);
+        bool ok = lb < bt_width && req >= 0;
+        int64_t blk = ok ? block_table[static_cast<int64_t>(req) * bt_width + lb] : 0;
+        ok = ok && blk >= 0 && blk < num_blocks;
+        if (!ok) blk = 0;
+        const int64_t src_row = blk * block_size + slot;
+        copy_row(k_cache + src_row * kvec, ws_k + static_cast<int64_t>(w) * kvec, kvec, ok);
+        copy_row(v_cache + src_row * vvec, ws_v + static_cast<int64_t>(w) * vvec, vvec, ok);
+    }
+}
+
+int grid_for(int64_t work, int64_t per_block, int64_t cap) {
+    int64_t g = (work + per_block - 1) / per_block;
+    if (g < 1) g = 1;
+    if (g > cap) g = cap;
+    return static_cast<int>(g);
+}
+
+}  // namespace
+
+int launch_init_partial(bf16_t* out, float* lse, int64_t lse_stride, int64_t row_begin, int64_t row_end,
+                        int32_t heads, int32_t head_dim, hipStream_t stream) {
+    const int64_t rows = row_end - row_begin;
+    if (rows <= 0) return MLA_OK;
+    const int64_t vpt = static_cast<int64_t>(heads) * head_dim / 8;
+    uint4* o = reinterpret_cast<uint4*>(out + row_begin * heads * head_dim);
+    const int grid = grid_for(rows * vpt, kThreads * 4, 8192);
+    TimedLaunch timed(MLA_KERNEL_INIT, stream);
+    hipLaunchKernelGGL(init_partial_kernel, dim3(grid), dim3(kThreads), 0, stream, o, lse, lse_stride, row_begin,
+                       rows, heads, vpt);
+    return hip_status(hipGetLastError());
+}
+
+int launch_merge(bf16_t* out, float* out_lse, const bf16_t* p_out, const float* p_lse, const bf16_t* s_out,
+                 const float* s_lse, int64_t tokens, int32_t heads, int32_t head_dim, int64_t out_stride,
+                 int64_t p_stride, int64_t s_stride, int64_t prefix_num_tokens, hipStream_t stream) {
+    if (tokens <= 0) return MLA_OK;
+    MergeArgs a{reinterpret_cast<uint4*>(out), out_lse, reinterpret_cast<const uint4*>(p_out), p_lse,
+                reinterpret_cast<const uint4*>(s_out), s_lse, tokens, heads, head_dim / 8, out_stride, p_stride,
+                s_stride, prefix_num_tokens};
+    TimedLaunch timed(MLA_KERNEL_MERGE, stream);
+    if (head_dim == 128) {
+        dim3 grid(static_cast<unsigned>((tokens + kMergeTokens - 1) / kMergeTokens),
+                  static_cast<unsigned>((heads + kMergeHeads - 1) / kMergeHeads));
+        hipLaunchKernelGGL(merge_kernel_d128, grid, dim3(kThreads), 0, stream, a);
+    } else {
+        const int grid = grid_for(tokens * heads * (head_dim / 8), kThreads, 16384);
+        hipLaunchKernelGGL(merge_kernel_generic, dim3(grid), dim3(kThreads), 0, stream, a);
+    }
+    return hip_status(hipGetLastError());
+}
+
+int launch_gather(const bf16_t* k_cache, const bf16_t* v_cache, int64_t num_blocks, int32_t block_size,
+                  int32_t heads, const int32_t* block_table, int32_t bt_width, const int32_t* e_req,
+                  const int32_t* e_start, const int32_t* e_off, int32_t n_entries, int32_t num_rows,
+                  bf16_t* ws_k, bf16_t* ws_v, hipStream_t stream) {
+    if (num_rows <= 0 || n_entries <= 0) return MLA_OK;
+    const unsigned grid = static_cast<unsigned>((num_rows + kGatherRows - 1) / kGatherRows);
+    TimedLaunch timed(MLA_KERNEL_GATHER, stream);
+    hipLaunchKernelGGL(gather_kernel, dim3(grid), dim3(kThreads), 0, stream,
+                       reinterpret_cast<const uint4*>(k_cache), reinterpret_cast<const uint4*>(v_cache), num_blocks,
+                       block_size, heads, block_table, bt_width, e_req, e_start, e_off, n_entries, num_rows,
+                       reinterpret_cast<uint4*>(ws_k), reinterpret_cast<uint4*>(ws_v));
+    return hip_status(hipGetLastError());
+}
+
+}  // namespace mla
+
+// ----------------------------------------------------------------------------
+// C ABI
+
+extern "C" {
+
+int mla_init_context_partial(void* out, float* lse, int64_t lse_head_stride, int64_t row_begin, int64_t row_end,
+                             int32_t num_heads, int32_t head_dim, void* stream) {
+    if (row_begin < 0 || row_end < row_begin || num_heads < 1 || head_dim < 8 || head_dim % 8 != 0)
+        return MLA_ERR_INVALID_ARG;
+    if (row_end == row_begin) return MLA_OK;
+    if (out == nullptr || lse == nullptr || !mla::aligned16(out) || lse_head_stride < row_end)
+        return MLA_ERR_INVALID_ARG;
+    return mla::launch_init_partial(static_cast<mla::bf16_t*>(out), lse, lse_head_stride, row_begin, row_end,
+                                    num_heads, head_dim, static_cast<hipStream_t>(stream));
+}
+
+int mla_merge_attn_states(void* out, float* out_lse, const void* prefix_out, const float* prefix_lse,
+                          const void* suffix_out, const float* suffix_lse, int64_t num_tokens, int32_t num_heads,
+                          int32_t head_dim, int64_t out_lse_stride, int64_t prefix_lse_stride,
+                          int64_t suffix_lse_stride, int64_t prefix_num_tokens, void* stream) {
+    if (num_tokens < 0 || num_heads < 1 || head_dim < 8 || head_dim % 8 != 0 || prefix_num_tokens < 0)
+        return MLA_ERR_INVALID_ARG;
+    if (num_tokens == 0) return MLA_OK;
+    if (out == nullptr || suffix_out == nullptr || suffix_lse == nullptr) return MLA_ERR_INVALID_ARG;
+    if (prefix_num_tokens > 0 && (prefix_out == nullptr || prefix_lse == nullptr)) return MLA_ERR_INVALID_ARG;
+    if (!mla::aligned16(out) || !mla::aligned16(suffix_out) || (prefix_out && !mla::aligned16(prefix_out)))
+        return MLA_ERR_INVALID_ARG;
+    if (suffix_lse_stride < num_tokens || (prefix_num_tokens > 0 && prefix_lse_stride < num_tokens) ||
+        (out_lse != nullptr && out_lse_stride < num_tokens))
+        return MLA_ERR_INVALID_ARG;
+    return mla::launch_merge(static_cast<mla::bf16_t*>(out), out_lse, static_cast<const mla::bf16_t*>(prefix_out),
+                             prefix_lse, static_cast<const mla::bf16_t*>(suffix_out), suffix_lse, num_tokens,
+                             num_heads, head_dim, out_lse_stride, prefix_lse_stride, suffix_lse_stride,
+                             prefix_num_tokens, static_cast<hipStream_t>(stream));
+}
+
+int mla_gather_context(const void* k_cache, const void* v_cache, int64_t num_blocks, int32_t block_size,
+                       int32_t num_heads, const int32_t* block_table, int32_t block_table_width,
+                       const int32_t* entry_request, const int32_t* entry_starts, const int32_t* entry_row_offsets,
+                       int32_t num_entries, int32_t num_rows, void* ws_k, void* ws_v, void* stream) {
+    if (num_blocks < 0 || block_size < 1 || num_heads < 1 || block_table_width < 0 || num_entries < 0 ||
+        num_rows < 0)
+        return MLA_ERR_INVALID_ARG;
+    if (num_rows == 0) return MLA_OK;
+    if (num_entries == 0 || k_cache == nullptr || v_cache == nullptr || block_table == nullptr ||
+        entry_request == nullptr || entry_starts == nullptr || entry_row_offsets == nullptr || ws_k == nullptr ||
+        ws_v == nullptr)
+        return MLA_ERR_INVALID_ARG;
+    if (!mla::aligned16(k_cache) || !mla::aligned16(v_cache) || !mla::aligned16(ws_k) || !mla::aligned16(ws_v))
+        return MLA_ERR_INVALID_ARG;
+    return mla::launch_gather(static_cast<const mla::bf16_t*>(k_cache), static_cast<const mla::bf16_t*>(v_cache),
+                              num_blocks, block_size, num_heads, block_table, block_table_width, entry_request,
+                              entry_starts, entry_row_offsets, num_entries, num_rows,
+                              static_cast<mla::bf16_t*>(ws_k), static_cast<mla::bf16_t*>(ws_v),
+                              static_cast<hipStream_t>(stream));
+}
+
+}  // extern "C"

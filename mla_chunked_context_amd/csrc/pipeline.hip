@@ -1,0 +1,301 @@
+// Chunked-context prefill driver (the _compute_prefill_context loop of the
+// vLLM PR #50613 digest, 实现拆解 item 3, plus the final merge of the PR
+// #36540 digest), native and stream-ordered:
+//
+//   host:   plan chunks, build per-chunk device metadata, one H2D upload
+//   device: init the partial rows of requests without context (0, -inf)
+//           for each chunk:
+//             gather its context rows into the workspace
+//             attention of its requests' queries against their rows; rows no
+//             earlier chunk wrote go straight into the context partial, the
+//             first request of a continuation chunk goes to a temporary and is
+//             LSE-merged into the partial (accumulate_mla_context_chunk)
+//           causal suffix attention over the new tokens
+//           merge_attn_states(partial, suffix, prefix_num_tokens) -> out
+//
+// A single chunk that covers every token (the digest's early exit when one
+// chunk covers all context) needs neither the init nor any accumulate: its
+// attention output is the partial.
+#include <algorithm>
+#include <array>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <vector>
+
+#include "device.h"
+#include "planner.h"
+
+namespace mla {
+
+namespace {
+
+constexpr int64_t kAlign = 256;
+
+int64_t round_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
+
+struct Plan {
+    std::vector<mla_chunk_desc> chunks;
+    std::vector<int32_t> starts, lens;
+};
+
+struct VecSink : PlanSink {
+    Plan* p;
+    void chunk(const mla_chunk_desc& c) override { p->chunks.push_back(c); }
+    void entry(int32_t s, int32_t n) override {
+        p->starts.push_back(s);
+        p->lens.push_back(n);
+    }
+    int32_t entries_so_far() const override { return static_cast<int32_t>(p->starts.size()); }
+};
+
+// Device metadata of one chunk, as offsets (in int32 elements) into the meta block.
+struct ChunkMeta {
+    int64_t e_req, e_start, e_off, cu_q;
+};
+
+struct Layout {
+    int64_t ws_k, ws_v, part_out, part_lse, suf_out, suf_lse, tmp_out, tmp_lse, meta;
+    int64_t total;
+    int64_t tmp_rows;   // rows of the continuation temporary
+    int64_t meta_ints;  // int32 elements of metadata
+};
+
+struct Problem {
+    Plan plan;
+    std::vector<int32_t> meta;  // host image of the device metadata
+    std::vector<ChunkMeta> cmeta;
+    int64_t suffix_cu;          // offset of the suffix query_start_loc
+    int64_t tokens = 0;
+    int32_t max_q = 0;
+    int64_t prefix_num_tokens = 0;
+    std::vector<int32_t> empty;  // pairs
+    Layout lay{};
+};
+
+int build_problem(const mla_chunked_prefill_params& p, Problem& pb) {
+    const int32_t n = p.num_requests;
+    VecSink sink;
+    sink.p = &pb.plan;
+    int st = plan_chunks(p.context_lens, p.query_lens, n, p.workspace_rows, p.max_context_chunk, p.split_alignment,
+                         sink);
+    if (st != MLA_OK) return st;
+    int32_t n_empty = 0;
+    st = token_info(p.context_lens, p.query_lens, n, &pb.prefix_num_tokens, nullptr, 0, &n_empty);
+    if (st != MLA_OK && st != MLA_ERR_CAPACITY) return st;
+    pb.empty.assign(2 * static_cast<size_t>(n_empty), 0);
+    st = token_info(p.context_lens, p.query_lens, n, &pb.prefix_num_tokens, pb.empty.data(), n_empty, &n_empty);
+    if (st != MLA_OK) return st;
+
+    std::vector<int64_t> qsl(n + 1, 0);
+    for (int32_t r = 0; r < n; ++r) {
+        qsl[r + 1] = qsl[r] + p.query_lens[r];
+        pb.max_q = std::max(pb.max_q, p.query_lens[r]);
+    }
+    pb.tokens = qsl[n];
+
+    // metadata image: per chunk e_req[n], e_start[n], e_off[n+1], cu_q[n+1]
+    int64_t tmp_rows = 0;
+    for (const auto& c : pb.plan.chunks) {
+        ChunkMeta m{};
+        const int32_t ne = c.num_entries;
+        m.e_req = static_cast<int64_t>(pb.meta.size());
+        for (int32_t i = 0; i < ne; ++i) pb.meta.push_back(c.request_begin + i);
+        m.e_start = static_cast<int64_t>(pb.meta.size());
+        for (int32_t i = 0; i < ne; ++i) pb.meta.push_back(pb.plan.starts[c.entry_begin + i]);
+        m.e_off = static_cast<int64_t>(pb.meta.size());
+        int32_t off = 0;
+        pb.meta.push_back(0);
+        for (int32_t i = 0; i < ne; ++i) {
+            off += pb.plan.lens[c.entry_begin + i];
+            pb.meta.push_back(off);
+        }
+        m.cu_q = static_cast<int64_t>(pb.meta.size());
+        for (int32_t i = 0; i <= ne; ++i)
+            pb.meta.push_back(static_cast<int32_t>(qsl[c.request_begin + i] - qsl[c.request_begin]));
+        pb.cmeta.push_back(m);
+        if (c.is_continuation) tmp_rows = std::max<int64_t>(tmp_rows, p.query_lens[c.request_begin]);
+    }
+    pb.suffix_cu = static_cast<int64_t>(pb.meta.size());
+    for (int32_t r = 0; r <= n; ++r) pb.meta.push_back(static_cast<int32_t>(qsl[r]));
+
+    // scratch layout
+    const int64_t H = p.num_heads, T = pb.tokens, W = p.workspace_rows;
+    Layout& L = pb.lay;
+    int64_t o = 0;
+    auto take = [&](int64_t bytes) {
+        const int64_t at = o;
+        o = round_up(o + std::max<int64_t>(bytes, 0), kAlign);
+        return at;
+    };
+    L.ws_k = take(W * H * kDk * 2);
+    L.ws_v = take(W * H * kDv * 2);
+    L.part_out = take(T * H * kDv * 2);
+    L.part_lse = take(H * T * 4);
+    L.suf_out = take(T * H * kDv * 2);
+    L.suf_lse = take(H * T * 4);
+    L.tmp_rows = tmp_rows;
+    L.tmp_out = take(tmp_rows * H * kDv * 2);
+    L.tmp_lse = take(H * tmp_rows * 4);
+    L.meta_ints = static_cast<int64_t>(pb.meta.size());
+    L.meta = take(L.meta_ints * 4);
+    L.total = o;
+    return MLA_OK;
+}
+
+// Pinned staging for the metadata upload.  A slot is reused only after the
+// copy that last read it has completed (its event), so calls can overlap.
+struct StagingSlot {
+    void* host = nullptr;
+    size_t cap = 0;
+    hipEvent_t ev = nullptr;
+    bool pending = false;
+};
+struct DevicePool {
+    std::array<StagingSlot, 4> slots;
+    int next = 0;
+};
+std::mutex g_pool_mu;
+std::map<int, DevicePool> g_pools;
+
+int upload(const void* src, size_t bytes, void* dst, hipStream_t stream) {
+    if (bytes == 0) return MLA_OK;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return MLA_ERR_HIP;
+    std::lock_guard<std::mutex> lock(g_pool_mu);
+    DevicePool& pool = g_pools[dev];
+    StagingSlot& s = pool.slots[pool.next];
+    pool.next = (pool.next + 1) % static_cast<int>(pool.slots.size());
+    if (s.pending) {
+        if (hipEventSynchronize(s.ev) != hipSuccess) return MLA_ERR_HIP;
+        s.pending = false;
+    }
+    if (s.ev == nullptr && hipEventCreateWithFlags(&s.ev, hipEventDisableTiming) != hipSuccess) return MLA_ERR_HIP;
+    if (s.cap < bytes) {
+        if (s.host != nullptr) hipHostFree(s.host);
+        s.host = nullptr;
+        s.cap = 0;
+        const size_t cap = std::max<size_t>(bytes * 2, 1 << 16);
+        if (hipHostMalloc(&s.host, cap, hipHostMallocDefault) != hipSuccess) return MLA_ERR_HIP;
+        s.cap = cap;
+    }
+    std::memcpy(s.host, src, bytes);
+    if (hipMemcpyAsync(dst, s.host, bytes, hipMemcpyHostToDevice, stream) != hipSuccess) return MLA_ERR_HIP;
+    if (hipEventRecord(s.ev, stream) != hipSuccess) return MLA_ERR_HIP;
+    s.pending = true;
+    return MLA_OK;
+}
+
+int check_params(const mla_chunked_prefill_params* p) {
+    if (p == nullptr) return MLA_ERR_INVALID_ARG;
+    if (p->num_requests < 0 || p->num_heads < 1 || p->block_size < 1 || p->block_table_width < 0 ||
+        p->num_blocks < 0 || p->workspace_rows < 1 || p->split_alignment < 1)
+        return MLA_ERR_INVALID_ARG;
+    if (!(p->scale > 0.f) || !std::isfinite(p->scale)) return MLA_ERR_INVALID_ARG;
+    if (p->num_requests > 0 && (p->context_lens == nullptr || p->query_lens == nullptr)) return MLA_ERR_INVALID_ARG;
+    return MLA_OK;
+}
+
+#define MLA_TRY(expr)                     \
+    do {                                  \
+        const int st_ = (expr);           \
+        if (st_ != MLA_OK) return st_;    \
+    } while (0)
+
+}  // namespace
+
+}  // namespace mla
+
+extern "C" {
+
+int mla_chunked_prefill_scratch_size(const mla_chunked_prefill_params* params, int64_t* bytes) {
+    if (bytes == nullptr) return MLA_ERR_INVALID_ARG;
+    MLA_TRY(mla::check_params(params));
+    mla::Problem pb;
+    MLA_TRY(mla::build_problem(*params, pb));
+    *bytes = pb.lay.total;
+    return MLA_OK;
+}
+
+int mla_chunked_prefill(const mla_chunked_prefill_params* params, void* stream_v) {
+    using namespace mla;
+    MLA_TRY(check_params(params));
+    const mla_chunked_prefill_params& p = *params;
+    Problem pb;
+    MLA_TRY(build_problem(p, pb));
+    const int64_t T = pb.tokens;
+    const int32_t H = p.num_heads;
+    if (T == 0) return MLA_OK;
+    if (p.q == nullptr || p.k_new == nullptr || p.v_new == nullptr || p.out == nullptr || p.scratch == nullptr)
+        return MLA_ERR_INVALID_ARG;
+    if (!aligned16(p.q) || !aligned16(p.k_new) || !aligned16(p.v_new) || !aligned16(p.out) ||
+        (reinterpret_cast<uintptr_t>(p.scratch) % kAlign) != 0)
+        return MLA_ERR_INVALID_ARG;
+    if (!pb.plan.chunks.empty()) {
+        if (p.k_cache == nullptr || p.v_cache == nullptr || p.block_table == nullptr || !aligned16(p.k_cache) ||
+            !aligned16(p.v_cache))
+            return MLA_ERR_INVALID_ARG;
+    }
+    if (p.scratch_bytes < pb.lay.total) return MLA_ERR_CAPACITY;
+
+    hipStream_t stream = static_cast<hipStream_t>(stream_v);
+    char* base = static_cast<char*>(p.scratch);
+    const Layout& L = pb.lay;
+    bf16_t* ws_k = reinterpret_cast<bf16_t*>(base + L.ws_k);
+    bf16_t* ws_v = reinterpret_cast<bf16_t*>(base + L.ws_v);
+    bf16_t* part_out = reinterpret_cast<bf16_t*>(base + L.part_out);
+    float* part_lse = reinterpret_cast<float*>(base + L.part_lse);
+    bf16_t* suf_out = reinterpret_cast<bf16_t*>(base + L.suf_out);
+    float* suf_lse = reinterpret_cast<float*>(base + L.suf_lse);
+    bf16_t* tmp_out = reinterpret_cast<bf16_t*>(base + L.tmp_out);
+    float* tmp_lse = reinterpret_cast<float*>(base + L.tmp_lse);
+    int32_t* meta = reinterpret_cast<int32_t*>(base + L.meta);
+
+    MLA_TRY(upload(pb.meta.data(), pb.meta.size() * sizeof(int32_t), meta, stream));
+
+    const bf16_t* q = static_cast<const bf16_t*>(p.q);
+    const int64_t qrow = static_cast<int64_t>(H) * kDk;
+    const int64_t orow = static_cast<int64_t>(H) * kDv;
+
+    // context partial of requests without context (only rows the final merge reads)
+    for (size_t i = 0; i + 1 < pb.empty.size(); i += 2) {
+        const int64_t b = pb.empty[i], e = std::min<int64_t>(pb.empty[i + 1], pb.prefix_num_tokens);
+        if (b < e) MLA_TRY(launch_init_partial(part_out, part_lse, T, b, e, H, kDv, stream));
+    }
+
+    for (size_t ci = 0; ci < pb.plan.chunks.size(); ++ci) {
+        const mla_chunk_desc& c = pb.plan.chunks[ci];
+        const ChunkMeta& m = pb.cmeta[ci];
+        MLA_TRY(launch_gather(static_cast<const bf16_t*>(p.k_cache), static_cast<const bf16_t*>(p.v_cache),
+                              p.num_blocks, p.block_size, H, p.block_table, p.block_table_width, meta + m.e_req,
+                              meta + m.e_start, meta + m.e_off, c.num_entries, c.num_rows, ws_k, ws_v, stream));
+        const bf16_t* qc = q + c.token_begin * qrow;
+        bf16_t* pc = part_out + c.token_begin * orow;
+        float* lc = part_lse + c.token_begin;
+        int32_t first_direct = 0;
+        if (c.is_continuation) {
+            // the first request already holds the previous chunk's result
+            const int32_t q0 = p.query_lens[c.request_begin];
+            if (q0 > 0) {
+                MLA_TRY(launch_attention(qc, ws_k, ws_v, meta + m.cu_q, meta + m.e_off, 1, q0, H, p.scale, false,
+                                         tmp_out, tmp_lse, L.tmp_rows, stream));
+                MLA_TRY(launch_merge(pc, lc, pc, lc, tmp_out, tmp_lse, q0, H, kDv, T, T, L.tmp_rows, q0, stream));
+            }
+            first_direct = 1;
+        }
+        if (c.num_entries > first_direct) {
+            MLA_TRY(launch_attention(qc, ws_k, ws_v, meta + m.cu_q + first_direct, meta + m.e_off + first_direct,
+                                     c.num_entries - first_direct, c.max_query_len, H, p.scale, false, pc, lc, T,
+                                     stream));
+        }
+    }
+
+    const int32_t* scu = meta + pb.suffix_cu;
+    MLA_TRY(launch_attention(q, static_cast<const bf16_t*>(p.k_new), static_cast<const bf16_t*>(p.v_new), scu, scu,
+                             p.num_requests, pb.max_q, H, p.scale, true, suf_out, suf_lse, T, stream));
+    MLA_TRY(launch_merge(static_cast<bf16_t*>(p.out), p.out_lse, part_out, part_lse, suf_out, suf_lse, T, H, kDv,
+                         T, T, T, pb.prefix_num_tokens, stream));
+    return MLA_OK;
+}
+
+}  // extern "C"

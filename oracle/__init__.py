@@ -27,12 +27,12 @@ from .planner import (ChunkPlan, ContextChunk, ChunkedContextMetadata, aligned_s
 from .attention import gather_context_rows, attention_with_lse
 from .merge import (merge_states, merge_attn_states, init_mla_context_partial,
                     accumulate_mla_context_chunk)
-from .pipeline import chunked_prefill, direct_prefill
+from .pipeline import chunked_prefill, direct_prefill, direct_rows
 
 __all__ = [
     "ChunkPlan", "ContextChunk", "ChunkedContextMetadata", "aligned_split_len",
     "plan_mla_context_chunks", "build_mla_chunked_context_metadata", "build_chunked_context",
     "gather_context_rows", "attention_with_lse", "merge_states", "merge_attn_states",
     "init_mla_context_partial", "accumulate_mla_context_chunk", "chunked_prefill",
-    "direct_prefill",
+    "direct_prefill", "direct_rows",
 ]

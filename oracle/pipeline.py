@@ -119,3 +119,30 @@ def direct_prefill(q, k_new, v_new, k_cache, v_cache, block_table, block_size, c
             out[a:b, h, :] = (e @ v_all[:, h, :]) / l
             lse[h, a:b] = (m + np.log(l))[:, 0]
     return out, lse
+
+
+def direct_rows(q_rows, positions, k_ctx, v_ctx, k_new, v_new, scale):
+    """The definition for selected tokens of one request.
+
+    q_rows [n, H, dk]: the queries of the selected tokens; positions [n]: each
+    token's index among the request's new tokens; k_ctx/v_ctx [c, H, d]: the
+    request's context rows in order; k_new/v_new [>= max(positions)+1, H, d]:
+    its new tokens.  Token i attends to all c context rows and new tokens
+    0..positions[i].  Returns out [n, H, dv] and lse [H, n] (float64)."""
+    q_rows = np.asarray(q_rows, dtype=np.float64)
+    n, H = q_rows.shape[0], q_rows.shape[1]
+    c = k_ctx.shape[0]
+    out = np.zeros((n, H, v_new.shape[2]), dtype=np.float64)
+    lse = np.full((H, n), -np.inf, dtype=np.float64)
+    k_all = np.concatenate([np.asarray(k_ctx, dtype=np.float64), np.asarray(k_new, dtype=np.float64)], axis=0)
+    v_all = np.concatenate([np.asarray(v_ctx, dtype=np.float64), np.asarray(v_new, dtype=np.float64)], axis=0)
+    for i, pos in enumerate(positions):
+        visible = c + int(pos) + 1
+        for h in range(H):
+            s = scale * (k_all[:visible, h, :] @ q_rows[i, h, :])
+            m = s.max()
+            e = np.exp(s - m)
+            l = e.sum()
+            out[i, h, :] = (e @ v_all[:visible, h, :]) / l
+            lse[h, i] = m + np.log(l)
+    return out, lse

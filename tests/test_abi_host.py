@@ -1,0 +1,167 @@
+"""C ABI checks that need no GPU: the library loads and exports every symbol
+the header declares; the host planner matches the oracle bit for bit; bad
+arguments are rejected before any HIP call."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle as O
+import workloads as W
+from tests.conftest import ROOT
+
+mla = pytest.importorskip("mla_chunked_context_amd")
+
+
+def _declared_functions():
+    names = []
+    for fn in os.listdir(os.path.join(ROOT, "include")):
+        if fn.endswith(".h"):
+            text = open(os.path.join(ROOT, "include", fn)).read()
+            text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+            names += re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(mla_[a-z_0-9]+)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_every_declared_symbol_is_exported():
+    names = _declared_functions()
+    assert len(names) >= 11
+    lib = ctypes.CDLL(mla.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert sorted(mla.EXPORTED) == names
+
+
+def test_version_and_status_strings():
+    assert mla.mla_abi_version() == 1
+    assert mla.mla_status_string(0) == "ok"
+    assert "capacity" in mla.mla_status_string(2)
+
+
+def _oracle_plan(ctx, ql, w, a, m=None):
+    md = O.build_mla_chunked_context_metadata(O.plan_mla_context_chunks(ctx, w, m, a), ctx, ql)
+    return md
+
+
+def _assert_same_plan(ctx, ql, w, a, m=None):
+    chunks, starts, lens = mla.mla_plan_context_chunks(ctx, ql, w, m or 0, a)
+    md = _oracle_plan(ctx, ql, w, a, m)
+    assert len(chunks) == len(md.chunks)
+    for c, oc in zip(chunks, md.chunks):
+        assert (c["request_begin"], c["request_end"]) == oc.request_slice
+        assert (c["token_begin"], c["token_end"]) == oc.token_slice
+        e0, ne = c["entry_begin"], c["num_entries"]
+        assert starts[e0:e0 + ne].tolist() == oc.starts.tolist()
+        assert lens[e0:e0 + ne].tolist() == oc.seq_lens.tolist()
+        assert c["num_rows"] == oc.num_rows
+        assert c["max_seq_len"] == oc.max_seq_len
+        assert c["max_query_len"] == oc.max_query_len
+        assert bool(c["is_continuation"]) == oc.is_continuation
+    pnt, empty = mla.mla_prefill_token_info(ctx, ql)
+    assert pnt == md.prefix_num_tokens
+    assert empty == md.empty_token_slices
+
+
+def test_planner_printed_example(golden):
+    g = golden("tail_split_example.json")
+    chunks, starts, lens = mla.mla_plan_context_chunks(g["context_lens"], g["query_lens"], g["workspace_rows"], 0, 64)
+    got = [dict(starts=starts[c["entry_begin"]:c["entry_begin"] + c["num_entries"]].tolist(),
+                seq_lens=lens[c["entry_begin"]:c["entry_begin"] + c["num_entries"]].tolist(),
+                is_continuation=bool(c["is_continuation"])) for c in chunks]
+    assert got == g["chunks"]
+
+
+def test_planner_matches_oracle_named():
+    for wl in W.named_workloads().values():
+        _assert_same_plan(list(wl.context_lens), list(wl.query_lens), wl.workspace_rows, wl.split_alignment)
+
+
+def test_planner_matches_oracle_random():
+    for seed in range(10000):
+        wl = W.random_workload(seed, max_requests=10, max_ctx=500, max_q=50)
+        m = None
+        if seed % 4 == 1 and wl.workspace_rows // 2 >= wl.split_alignment:
+            m = wl.workspace_rows // 2
+        _assert_same_plan(list(wl.context_lens), list(wl.query_lens), wl.workspace_rows, wl.split_alignment, m)
+
+
+def test_planner_large_lens():
+    rng = np.random.default_rng(5)
+    for _ in range(200):
+        n = int(rng.integers(1, 64))
+        ctx = [0 if rng.random() < 0.1 else int(rng.integers(1, 200_000)) for _ in range(n)]
+        ql = [int(rng.integers(0, 4096)) for _ in range(n)]
+        a = int(rng.choice([16, 64, 256]))
+        w = int(rng.integers(a, 300_000))
+        _assert_same_plan(ctx, ql, w, a)
+
+
+def test_planner_rejects_bad_arguments():
+    with pytest.raises(mla.MlaError) as e:
+        mla.mla_plan_context_chunks([10], [1], 8, 0, 16)
+    assert e.value.status == mla.MLA_ERR_INVALID_ARG
+    for args in [([10], [1], 16, 0, 0), ([10], [1], 64, 8, 16), ([-1], [1], 64, 0, 16), ([3], [-2], 64, 0, 16)]:
+        with pytest.raises(mla.MlaError):
+            mla.mla_plan_context_chunks(*args)
+
+
+def test_planner_capacity_reporting():
+    ctx = (ctypes.c_int32 * 3)(768, 512, 512)
+    ql = (ctypes.c_int32 * 3)(3, 5, 7)
+    nc, ne = ctypes.c_int32(0), ctypes.c_int32(0)
+    one = (mla.ChunkDesc * 1)()
+    st = mla._plan(ctx, ql, 3, 1024, 0, 64, one, 1, ctypes.byref(nc), None, None, 0, ctypes.byref(ne))
+    # null entry arrays with capacity 0 are allowed; one chunk slot is too few
+    assert st == mla.MLA_ERR_CAPACITY and nc.value == 2 and ne.value == 4
+    s = (ctypes.c_int32 * 8)()
+    n = (ctypes.c_int32 * 8)()
+    st = mla._plan(ctx, ql, 3, 1024, 0, 64, one, 1, ctypes.byref(nc), s, n, 8, ctypes.byref(ne))
+    assert st == mla.MLA_ERR_CAPACITY and nc.value == 2 and ne.value == 4
+
+
+def test_device_calls_reject_bad_arguments_without_gpu():
+    """Argument checks run before any HIP call, so they work on a CPU-only host."""
+    f = mla._lib
+    # null pointers with work to do
+    assert f.mla_merge_attn_states(None, None, None, None, None, None, ctypes.c_int64(4), 2, 128, ctypes.c_int64(4),
+                                   ctypes.c_int64(4), ctypes.c_int64(4), ctypes.c_int64(4), None) == 1
+    # head_dim not a multiple of 8
+    assert f.mla_init_context_partial(ctypes.c_void_p(256), ctypes.c_void_p(256), ctypes.c_int64(8),
+                                      ctypes.c_int64(0), ctypes.c_int64(4), 2, 12, None) == 1
+    # misaligned output pointer
+    assert f.mla_init_context_partial(ctypes.c_void_p(258), ctypes.c_void_p(256), ctypes.c_int64(8),
+                                      ctypes.c_int64(0), ctypes.c_int64(4), 2, 16, None) == 1
+    # non-positive scale
+    assert f.mla_context_chunk_attn(ctypes.c_void_p(256), ctypes.c_void_p(256), ctypes.c_void_p(256),
+                                    ctypes.c_void_p(256), ctypes.c_void_p(256), 1, 4, 2, ctypes.c_float(0.0),
+                                    ctypes.c_void_p(256), ctypes.c_void_p(256), ctypes.c_int64(4), None) == 1
+    # gather with rows but no entries
+    assert f.mla_gather_context(ctypes.c_void_p(256), ctypes.c_void_p(256), ctypes.c_int64(4), 16, 2,
+                                ctypes.c_void_p(256), 4, ctypes.c_void_p(256), ctypes.c_void_p(256),
+                                ctypes.c_void_p(256), 0, 8, ctypes.c_void_p(256), ctypes.c_void_p(256), None) == 1
+    # empty work is a no-op success, no HIP call
+    assert f.mla_merge_attn_states(None, None, None, None, None, None, ctypes.c_int64(0), 2, 128, ctypes.c_int64(0),
+                                   ctypes.c_int64(0), ctypes.c_int64(0), ctypes.c_int64(0), None) == 0
+
+
+def test_prefill_scratch_size_and_param_checks():
+    wl = W.named_workloads()[5]
+    p = mla.ChunkedPrefillParams()
+    ctx = np.asarray(wl.context_lens, dtype=np.int32)
+    ql = np.asarray(wl.query_lens, dtype=np.int32)
+    p.context_lens, p.query_lens, p.num_requests = ctx.ctypes.data, ql.ctypes.data, 4
+    p.num_heads, p.block_size, p.block_table_width, p.num_blocks = 128, 64, 2048, 8192
+    p.scale, p.workspace_rows, p.split_alignment = wl.scale, wl.workspace_rows, 64
+    n = mla.mla_chunked_prefill_scratch_size(p)
+    T, H, Wr = 32768, 128, 65536
+    expect_min = Wr * H * 640 + 2 * T * H * (256 + 4) + 8192 * H * 260
+    assert expect_min <= n <= expect_min + 64 * 4096
+    p.scratch_bytes = n - 1
+    # too-small scratch is caught before any HIP call... after pointer checks
+    with pytest.raises(mla.MlaError):
+        mla.mla_chunked_prefill(p, stream=0)
+    p.split_alignment = 0
+    with pytest.raises(mla.MlaError):
+        mla.mla_chunked_prefill_scratch_size(p)

@@ -152,3 +152,18 @@ def test_pins_catch_missing_threshold(monkeypatch):
     real = OP.merge_attn_states
     monkeypatch.setattr(OP, "merge_attn_states", lambda po, pl, so, sl, k: real(po, pl, so, sl, 0))
     assert not _pins_pass()
+
+
+def test_direct_rows_matches_direct_prefill():
+    wl = W.named_workloads()[1]
+    b = W.make_batch(wl)
+    a = _arrays(b)
+    d_out, d_lse = O.direct_prefill(*a, wl.scale)
+    f = W.to_f64
+    # request 1: context 512 rows, 5 new tokens starting at token 3
+    table = b.block_table.numpy()
+    rows = [f(b.k_cache)[table[1][p // 64], p % 64] for p in range(512)]
+    vrows = [f(b.v_cache)[table[1][p // 64], p % 64] for p in range(512)]
+    out, lse = O.direct_rows(f(b.q)[[4, 7]], [1, 4], np.stack(rows), np.stack(vrows), f(b.k_new)[3:8],
+                             f(b.v_new)[3:8], wl.scale)
+    assert np.allclose(out, d_out[[4, 7]], atol=1e-13) and np.allclose(lse, d_lse[:, [4, 7]], atol=1e-13)

@@ -94,8 +94,11 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="long_context",
                     choices=["tiny", "empty_context_stress", "homogeneous", "heterogeneous", "long_context"])
-    ap.add_argument("--cpu-sample-queries", type=int, default=1024)
+    ap.add_argument("--cpu-sample-queries", type=int, default=8192)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibration-copy-mb", type=int, default=0,
+                    help="after timing, run one elementwise copy (negation) of this many MiB of bf16 so that "
+                         "hardware byte counters can be scaled against a kernel of known traffic")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print(f"bench.py runs on one GPU only: the chunked-prefill path here is single-GPU "
@@ -178,6 +181,15 @@ def main():
                      "avg_launch_ms": round(ms_ca / n_ca, 4) if n_ca else None},
         "kernels": kernels,
     }
+    if args.calibration_copy_mb > 0:
+        n = args.calibration_copy_mb * (1 << 20) // 2
+        src = torch.ones(n, dtype=torch.bfloat16, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        res["calibration_copy_bytes"] = {"read": n * 2, "write": n * 2}
+        del src, dst
     del scratch
     torch.cuda.empty_cache()
     if not args.no_cpu_baseline:

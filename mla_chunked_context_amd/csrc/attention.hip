@@ -1,6 +1,6 @@
 // Varlen attention with LSE for MLA prefill on gfx950 (qk dim 192, v dim 128).
 //
-// One kernel serves both attention steps of the chunked prefill:
+// One kernel body serves both attention steps of the chunked prefill:
 //   * chunk attention (non-causal): the prefill queries of each request in a
 //     chunk against that request's gathered context rows
 //     (run_prefill_context_chunk, vLLM PR #50613 digest, 实现拆解 item 4);
@@ -10,18 +10,22 @@
 // in fp32, stored head-major.
 //
 // Work decomposition
-//   A workgroup owns 128 queries of one (sequence, head): 4 waves x 32 queries.
-//   Keys stream through LDS in tiles of 64 (K row-major, V transposed), shared
-//   by the 4 waves; the next tile's global loads are in flight while the
-//   current tile is computed.  Workgroup ids are remapped so that the query
-//   tiles of one (sequence, head) run on the same XCD and share its L2.
+//   A workgroup owns 256 queries of one (sequence, head): 8 waves x 32
+//   queries, two waves per SIMD.  Keys stream through LDS in tiles of 64 (K
+//   row-major, V transposed), double-buffered: the next tile's global loads
+//   are in flight while the current tile is computed, and one barrier per
+//   tile separates the write of one buffer from the reads of the other.
+//   Workgroup ids are remapped so that the query tiles of one (sequence, head)
+//   run on the same XCD and share its L2.
+//   K/V tiles are read with buffer loads whose descriptor covers exactly the
+//   valid keys of the tile: keys past the end read as zero without branches,
+//   and are masked to -inf before the softmax.
 //
 // MFMA formulation (v_mfma_f32_32x32x16_bf16, wave64)
 //   S^T = K Q^T : A = K tile rows from LDS, B = Q fragments held in registers.
 //     The accumulator gives each lane one query column (lane & 31) and 16 of
 //     each 32-key block's rows, so the running max / sum of a query live in
-//     one lane pair (lane, lane ^ 32): no cross-lane reductions except one
-//     swap per tile for the max.
+//     one lane pair (lane, lane ^ 32), combined with one v_permlane32_swap.
 //   O^T = V^T P^T : B = P^T taken directly from the S^T accumulators
 //     (converted to bf16); A = V^T from LDS.  The 8 keys a lane contributes
 //     to one 16-key step are not contiguous in key order (accumulator rows
@@ -31,7 +35,11 @@
 //   the products are correct whatever order the hardware assigns to k.
 //
 // Softmax: base-2 exponentials with the scale folded in, p = 2^(s*c - m),
-// c = scale * log2(e); the LSE is converted back to natural log at the end.
+// c = scale * log2(e).  The reference max m of a query is raised only when a
+// tile's max exceeds it by more than 2^8 (then O and the sum are rescaled);
+// otherwise the stale m is kept, so p <= 256, which fp32 sums and bf16 P
+// represent with the same relative precision.  The LSE is m + log2(sum)
+// converted to natural log at the end.
 #include <cmath>
 
 #include "device.h"
@@ -42,17 +50,25 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kThreads = 256;
-constexpr int kWaves = 4;
+constexpr int kWaves = 8;
+constexpr int kThreads = kWaves * 64;
 constexpr int kQPerWave = 32;
 constexpr int kBlockM = kWaves * kQPerWave;  // queries per workgroup
 constexpr int kBlockN = 64;                  // keys per tile
 constexpr int kKStride = kDk + 8;            // K tile LDS row stride (elements): 400 B
 constexpr int kVtStride = kBlockN + 8;       // V^T tile LDS row stride (elements): 144 B
 constexpr int kKVecPerRow = kDk / 8;         // 24 16-byte vectors per K row
-constexpr int kKLoads = kBlockN * kKVecPerRow / kThreads;  // 6 per thread
-constexpr int kVLoads = 4;                                  // 4 keys x 8 dims per thread
+constexpr int kKLoads = kBlockN * kKVecPerRow / kThreads;  // 3 per thread
+constexpr int kVLoads = 2;                                  // 2 keys x 8 dims per thread
+constexpr int kKTileElems = kBlockN * kKStride;
+constexpr int kVtTileElems = kDv * kVtStride;
+constexpr float kRescaleThreshold = 8.0f;  // log2 units
+constexpr int kBufferConfig = 0x00020000;  // dword 3 of a raw buffer descriptor on gfx9
+
+static_assert(kBlockN * kKVecPerRow == kKLoads * kThreads, "K tile must split evenly over threads");
+static_assert(kBlockN / 2 * (kDv / 8) == kThreads, "V tile mapping: 32 key pairs x 16 dim groups");
 
 struct AttnArgs {
     const bf16_t* q;
@@ -81,6 +97,16 @@ __device__ __forceinline__ int vt_pos(int key) {
     return (key & ~12) | ((key & 4) << 1) | ((key & 8) >> 1);
 }
 
+// x of this lane and of lane ^ 32, via one cross-half swap (no LDS).
+__device__ __forceinline__ float pair_max(float x) {
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+}
+
 // Workgroups are dealt to the 8 XCDs round-robin; map them so that each XCD
 // processes a contiguous range of logical tiles.
 __device__ __forceinline__ int32_t xcd_logical_tile(int32_t bid, int32_t total) {
@@ -90,10 +116,7 @@ __device__ __forceinline__ int32_t xcd_logical_tile(int32_t bid, int32_t total) 
 }
 
 template <bool kCausal>
-__global__ __launch_bounds__(kThreads, 2) void attention_kernel(AttnArgs a) {
-    __shared__ __attribute__((aligned(16))) bf16_t k_lds[kBlockN * kKStride];
-    __shared__ __attribute__((aligned(16))) bf16_t vt_lds[kDv * kVtStride];
-
+__device__ __forceinline__ void attention_body(const AttnArgs& a, bf16_t* k_lds, bf16_t* vt_lds) {
     const int32_t tile = xcd_logical_tile(blockIdx.x, a.total_tiles);
     int32_t qt = tile % a.q_tiles;
     const int32_t rest = tile / a.q_tiles;
@@ -124,7 +147,8 @@ __global__ __launch_bounds__(kThreads, 2) void attention_kernel(AttnArgs a) {
             a.q + (static_cast<int64_t>(q_begin + (q_valid ? q_row : 0)) * H + head) * kDk + g * 8);
 #pragma unroll
         for (int ks = 0; ks < kDk / 16; ++ks) {
-            uint4 x = q_valid ? qp[ks * 2] : make_uint4(0u, 0u, 0u, 0u);
+            uint4 x = make_uint4(0u, 0u, 0u, 0u);
+            if (q_valid) x = qp[ks * 2];
             qf[ks] = __builtin_bit_cast(bf16x8, x);
         }
     }
@@ -134,152 +158,160 @@ __global__ __launch_bounds__(kThreads, 2) void attention_kernel(AttnArgs a) {
     for (int db = 0; db < kDv / 32; ++db)
 #pragma unroll
         for (int r = 0; r < 16; ++r) o_acc[db][r] = 0.f;
-    float m_run = -INFINITY;  // running max of s * c over this lane pair's query
-    float l_run = 0.f;        // this lane's share of the running sum
+    float m_run = -INFINITY;  // reference max of s * c for this lane pair's query
+    float l_run = 0.f;        // this lane's share of the sum of 2^(s*c - m_run)
 
-    // ---- staging of one key tile: global -> registers -> LDS
-    uint4 kreg[kKLoads];
-    uint4 vreg[kVLoads];
-    const int vkq = tid & 15;  // keys 4*vkq .. 4*vkq+3 of the tile
-    const int vdc = tid >> 4;  // dims 8*vdc .. 8*vdc+7
+    // ---- tile staging: per-thread offsets are fixed; the tile base moves
+    const bf16_t* kseq = a.k + static_cast<int64_t>(k_begin) * H * kDk + static_cast<int64_t>(head) * kDk;
+    const bf16_t* vseq = a.v + static_cast<int64_t>(k_begin) * H * kDv + static_cast<int64_t>(head) * kDv;
+    const int32_t k_row_bytes = H * kDk * 2;
+    const int32_t v_row_bytes = H * kDv * 2;
+    int32_t k_goff[kKLoads], k_loff[kKLoads];
+#pragma unroll
+    for (int i = 0; i < kKLoads; ++i) {
+        const int vidx = tid + i * kThreads;
+        const int key = vidx / kKVecPerRow;
+        const int c = vidx - key * kKVecPerRow;
+        k_goff[i] = key * k_row_bytes + c * 16;
+        k_loff[i] = key * kKStride + c * 8;
+    }
+    const int vkp = tid & 31;  // keys 2*vkp, 2*vkp+1 of the tile
+    const int vdc = tid >> 5;  // dims 8*vdc .. 8*vdc+7
+    const int32_t v_goff = 2 * vkp * v_row_bytes + vdc * 16;
+    const int v_lpos = vt_pos(2 * vkp);
 
+    u32x4 kreg[kKLoads];
+    u32x4 vreg[kVLoads];
     auto load_tile = [&](int32_t k0) {
+        const int32_t keys = min(kBlockN, kv_end - k0);
+        const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<bf16_t*>(kseq + static_cast<int64_t>(k0) * H * kDk), 0, keys * k_row_bytes, kBufferConfig);
+        const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<bf16_t*>(vseq + static_cast<int64_t>(k0) * H * kDv), 0, keys * v_row_bytes, kBufferConfig);
 #pragma unroll
-        for (int i = 0; i < kKLoads; ++i) {
-            const int vidx = tid + i * kThreads;
-            const int key = vidx / kKVecPerRow;
-            const int c = vidx - key * kKVecPerRow;
-            const int32_t kr = k0 + key;
-            kreg[i] = kr < kv_end ? *reinterpret_cast<const uint4*>(
-                                        a.k + (static_cast<int64_t>(k_begin + kr) * H + head) * kDk + c * 8)
-                                  : make_uint4(0u, 0u, 0u, 0u);
-        }
+        for (int i = 0; i < kKLoads; ++i) kreg[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, k_goff[i], 0, 0);
 #pragma unroll
-        for (int u = 0; u < kVLoads; ++u) {
-            const int32_t kr = k0 + vkq * 4 + u;
-            vreg[u] = kr < kv_end ? *reinterpret_cast<const uint4*>(
-                                        a.v + (static_cast<int64_t>(k_begin + kr) * H + head) * kDv + vdc * 8)
-                                  : make_uint4(0u, 0u, 0u, 0u);
-        }
+        for (int u = 0; u < kVLoads; ++u)
+            vreg[u] = __builtin_amdgcn_raw_buffer_load_b128(rv, v_goff + u * v_row_bytes, 0, 0);
     };
-    auto store_tile = [&]() {
+    auto store_tile = [&](int buf) {
+        bf16_t* kl = k_lds + buf * kKTileElems;
+        bf16_t* vl = vt_lds + buf * kVtTileElems;
 #pragma unroll
-        for (int i = 0; i < kKLoads; ++i) {
-            const int vidx = tid + i * kThreads;
-            const int key = vidx / kKVecPerRow;
-            const int c = vidx - key * kKVecPerRow;
-            *reinterpret_cast<uint4*>(&k_lds[key * kKStride + c * 8]) = kreg[i];
-        }
-        // transpose 4 keys x 8 dims into 8 rows (dims) of 4 keys
-        const int pos = vt_pos(vkq * 4);
-        const uint32_t w[4][4] = {{vreg[0].x, vreg[0].y, vreg[0].z, vreg[0].w},
-                                  {vreg[1].x, vreg[1].y, vreg[1].z, vreg[1].w},
-                                  {vreg[2].x, vreg[2].y, vreg[2].z, vreg[2].w},
-                                  {vreg[3].x, vreg[3].y, vreg[3].z, vreg[3].w}};
+        for (int i = 0; i < kKLoads; ++i) *reinterpret_cast<u32x4*>(&kl[k_loff[i]]) = kreg[i];
+        // transpose 2 keys x 8 dims into 8 rows (dims) of 2 keys
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const uint32_t lo_e0 = (w[0][i] & 0xffffu) | (w[1][i] << 16);
-            const uint32_t hi_e0 = (w[2][i] & 0xffffu) | (w[3][i] << 16);
-            const uint32_t lo_e1 = (w[0][i] >> 16) | (w[1][i] & 0xffff0000u);
-            const uint32_t hi_e1 = (w[2][i] >> 16) | (w[3][i] & 0xffff0000u);
+            const uint32_t w0 = vreg[0][i], w1 = vreg[1][i];
             const int d0 = vdc * 8 + 2 * i;
-            *reinterpret_cast<uint2*>(&vt_lds[d0 * kVtStride + pos]) = make_uint2(lo_e0, hi_e0);
-            *reinterpret_cast<uint2*>(&vt_lds[(d0 + 1) * kVtStride + pos]) = make_uint2(lo_e1, hi_e1);
+            *reinterpret_cast<uint32_t*>(&vl[d0 * kVtStride + v_lpos]) = (w0 & 0xffffu) | (w1 << 16);
+            *reinterpret_cast<uint32_t*>(&vl[(d0 + 1) * kVtStride + v_lpos]) = (w0 >> 16) | (w1 & 0xffff0000u);
         }
     };
 
     const int32_t n_tiles = (kv_end + kBlockN - 1) / kBlockN;
+    const int32_t wave_last_q = qt * kBlockM + wave * kQPerWave + kQPerWave - 1;
     if (n_tiles > 0) {
         load_tile(0);
-        store_tile();
+        store_tile(0);
     }
     __syncthreads();
 
     for (int32_t t = 0; t < n_tiles; ++t) {
         const int32_t k0 = t * kBlockN;
+        const int buf = t & 1;
         if (t + 1 < n_tiles) load_tile(k0 + kBlockN);
 
-        // ---- S^T = K Q^T for two 32-key blocks
-        f32x16 s[2];
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
-            const bf16_t* krow = &k_lds[(kb * 32 + l32) * kKStride + g * 8];
-#pragma unroll
-            for (int ks = 0; ks < kDk / 16; ++ks) {
-                const bf16x8 af = *reinterpret_cast<const bf16x8*>(krow + ks * 16);
-                s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, qf[ks], s[kb], 0, 0, 0);
-            }
-        }
-
-        // ---- mask keys past the end (and above the diagonal when causal)
-        const bool need_mask = (k0 + kBlockN > kv_end) ||
-                               (kCausal && k0 + kBlockN - 1 > qt * kBlockM + wave * kQPerWave);
-        if (need_mask) {
+        // a causal wave whose queries all precede this tile has nothing to do
+        if (!kCausal || k0 <= wave_last_q) {
+            const bf16_t* kl = k_lds + buf * kKTileElems;
+            const bf16_t* vl = vt_lds + buf * kVtTileElems;
+            // ---- S^T = K Q^T for two 32-key blocks
+            f32x16 s[2];
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int32_t key = k0 + kb * 32 + (r >> 2) * 8 + g * 4 + (r & 3);
-                    const bool dead = key >= kv_end || (kCausal && key > q_row);
-                    if (dead) s[kb][r] = -INFINITY;
+                for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
+#pragma unroll
+            for (int ks = 0; ks < kDk / 16; ++ks)
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb) {
+                    const bf16x8 af =
+                        *reinterpret_cast<const bf16x8*>(&kl[(kb * 32 + l32) * kKStride + g * 8 + ks * 16]);
+                    s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, qf[ks], s[kb], 0, 0, 0);
                 }
-        }
 
-        // ---- online softmax (base 2), one query per lane pair
-        float mx = -INFINITY;
+            // ---- mask keys past the end (and above the diagonal when causal)
+            const bool need_mask = (k0 + kBlockN > kv_end) ||
+                                   (kCausal && k0 + kBlockN - 1 > qt * kBlockM + wave * kQPerWave);
+            if (need_mask) {
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+                for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float m_new = fmaxf(m_run, mx * a.scale_log2);
-        const float m_use = m_new == -INFINITY ? 0.f : m_new;
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-        m_run = m_new;
-        float psum = 0.f;
-        bf16x8 pb[2][2];
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int hh = 0; hh < 2; ++hh) {
-                uint32_t pk[4];
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const float p0 = __builtin_amdgcn_exp2f(fmaf(s[kb][hh * 8 + 2 * j], a.scale_log2, -m_use));
-                    const float p1 = __builtin_amdgcn_exp2f(fmaf(s[kb][hh * 8 + 2 * j + 1], a.scale_log2, -m_use));
-                    psum += p0 + p1;
-                    pk[j] = pack_bf16x2(p0, p1);
-                }
-                pb[kb][hh] = __builtin_bit_cast(bf16x8, make_uint4(pk[0], pk[1], pk[2], pk[3]));
+                    for (int r = 0; r < 16; ++r) {
+                        const int32_t key = k0 + kb * 32 + (r >> 2) * 8 + g * 4 + (r & 3);
+                        const bool dead = key >= kv_end || (kCausal && key > q_row);
+                        if (dead) s[kb][r] = -INFINITY;
+                    }
             }
-        l_run = l_run * alpha + psum;
-#pragma unroll
-        for (int db = 0; db < kDv / 32; ++db)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) o_acc[db][r] *= alpha;
 
-        // ---- O^T += V^T P^T
+            // ---- online softmax (base 2) with a lazily raised reference max
+            float mx = -INFINITY;
 #pragma unroll
-        for (int db = 0; db < kDv / 32; ++db) {
-            const bf16_t* vrow = &vt_lds[(db * 32 + l32) * kVtStride + g * 8];
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+            const float m_tile = pair_max(mx) * a.scale_log2;
+            const bool raise = m_tile > m_run + kRescaleThreshold;
+            if (__builtin_amdgcn_ballot_w64(raise) != 0) {
+                const float m_new = raise ? m_tile : m_run;
+                const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 0 when m_run is -inf
+                l_run *= alpha;
+#pragma unroll
+                for (int db = 0; db < kDv / 32; ++db)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) o_acc[db][r] *= alpha;
+                m_run = m_new;
+            }
+            const float m_use = m_run == -INFINITY ? 0.f : m_run;
+            bf16x8 pb[2][2];
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
                 for (int hh = 0; hh < 2; ++hh) {
-                    const bf16x8 af = *reinterpret_cast<const bf16x8*>(vrow + kb * 32 + hh * 16);
-                    o_acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, pb[kb][hh], o_acc[db], 0, 0, 0);
+                    uint32_t pk[4];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const float p0 =
+                            __builtin_amdgcn_exp2f(fmaf(s[kb][hh * 8 + 2 * j], a.scale_log2, -m_use));
+                        const float p1 =
+                            __builtin_amdgcn_exp2f(fmaf(s[kb][hh * 8 + 2 * j + 1], a.scale_log2, -m_use));
+                        l_run += p0 + p1;
+                        pk[j] = pack_bf16x2(p0, p1);
+                    }
+                    pb[kb][hh] = __builtin_bit_cast(bf16x8, make_uint4(pk[0], pk[1], pk[2], pk[3]));
                 }
+
+            // ---- O^T += V^T P^T (4 independent accumulator chains)
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+                    for (int db = 0; db < kDv / 32; ++db) {
+                        const bf16x8 af = *reinterpret_cast<const bf16x8*>(
+                            &vl[(db * 32 + l32) * kVtStride + g * 8 + kb * 32 + hh * 16]);
+                        o_acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, pb[kb][hh], o_acc[db], 0, 0, 0);
+                    }
         }
 
-        __syncthreads();
-        if (t + 1 < n_tiles) store_tile();
+        // the other buffer was last read before the previous barrier
+        if (t + 1 < n_tiles) store_tile(buf ^ 1);
         __syncthreads();
     }
 
     // ---- epilogue: normalise, write bf16 output rows and the LSE
-    const float l_tot = l_run + __shfl_xor(l_run, 32);
+    const float l_tot = pair_sum(l_run);
     if (!q_valid) return;
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     bf16_t* orow = a.out + (static_cast<int64_t>(q_begin + q_row) * H + head) * kDv + g * 4;
@@ -295,6 +327,19 @@ __global__ __launch_bounds__(kThreads, 2) void attention_kernel(AttnArgs a) {
         const float lse = l_tot > 0.f ? (m_run + log2f(l_tot)) * 0.69314718055994531f : -INFINITY;
         a.lse[head * a.lse_stride + q_begin + q_row] = lse;
     }
+}
+
+// Distinct entry points so that profiles separate the two steps.
+__global__ __launch_bounds__(kThreads, 1) void chunk_attention_kernel(AttnArgs a) {
+    __shared__ __attribute__((aligned(16))) bf16_t k_lds[2 * kKTileElems];
+    __shared__ __attribute__((aligned(16))) bf16_t vt_lds[2 * kVtTileElems];
+    attention_body<false>(a, k_lds, vt_lds);
+}
+
+__global__ __launch_bounds__(kThreads, 1) void suffix_attention_kernel(AttnArgs a) {
+    __shared__ __attribute__((aligned(16))) bf16_t k_lds[2 * kKTileElems];
+    __shared__ __attribute__((aligned(16))) bf16_t vt_lds[2 * kVtTileElems];
+    attention_body<true>(a, k_lds, vt_lds);
 }
 
 }  // namespace
@@ -321,9 +366,9 @@ int launch_attention(const bf16_t* q, const bf16_t* k, const bf16_t* v, const in
     a.scale_log2 = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
     TimedLaunch timed(causal ? MLA_KERNEL_SUFFIX_ATTN : MLA_KERNEL_CHUNK_ATTN, stream);
     if (causal)
-        hipLaunchKernelGGL(attention_kernel<true>, dim3(a.total_tiles), dim3(kThreads), 0, stream, a);
+        hipLaunchKernelGGL(suffix_attention_kernel, dim3(a.total_tiles), dim3(kThreads), 0, stream, a);
     else
-        hipLaunchKernelGGL(attention_kernel<false>, dim3(a.total_tiles), dim3(kThreads), 0, stream, a);
+        hipLaunchKernelGGL(chunk_attention_kernel, dim3(a.total_tiles), dim3(kThreads), 0, stream, a);
     return hip_status(hipGetLastError());
 }
 

@@ -41,6 +41,7 @@
 // represent with the same relative precision.  The LSE is m + log2(sum)
 // converted to natural log at the end.
 #include <cmath>
+#include <type_traits>
 
 #include "device.h"
 
@@ -211,21 +212,25 @@ __device__ __forceinline__ void attention_body(const AttnArgs& a, bf16_t* k_lds,
 
     const int32_t n_tiles = (kv_end + kBlockN - 1) / kBlockN;
     const int32_t wave_last_q = qt * kBlockM + wave * kQPerWave + kQPerWave - 1;
+    // per-lane LDS bases; every fragment read is base + a compile-time offset
+    const bf16_t* k_lane = k_lds + l32 * kKStride + g * 8;
+    const bf16_t* v_lane = vt_lds + l32 * kVtStride + g * 8;
     if (n_tiles > 0) {
         load_tile(0);
         store_tile(0);
     }
     __syncthreads();
 
-    for (int32_t t = 0; t < n_tiles; ++t) {
+    // one key tile: compute on LDS buffer `buf` (a compile-time constant so
+    // that the LDS reads use immediate offsets), stage the next tile into the
+    // other buffer, barrier
+    auto step = [&](int32_t t, auto buf_tag) {
+        constexpr int buf = decltype(buf_tag)::value;
         const int32_t k0 = t * kBlockN;
-        const int buf = t & 1;
         if (t + 1 < n_tiles) load_tile(k0 + kBlockN);
 
         // a causal wave whose queries all precede this tile has nothing to do
         if (!kCausal || k0 <= wave_last_q) {
-            const bf16_t* kl = k_lds + buf * kKTileElems;
-            const bf16_t* vl = vt_lds + buf * kVtTileElems;
             // ---- S^T = K Q^T for two 32-key blocks
             f32x16 s[2];
 #pragma unroll
@@ -236,8 +241,8 @@ __device__ __forceinline__ void attention_body(const AttnArgs& a, bf16_t* k_lds,
             for (int ks = 0; ks < kDk / 16; ++ks)
 #pragma unroll
                 for (int kb = 0; kb < 2; ++kb) {
-                    const bf16x8 af =
-                        *reinterpret_cast<const bf16x8*>(&kl[(kb * 32 + l32) * kKStride + g * 8 + ks * 16]);
+                    const bf16x8 af = *reinterpret_cast<const bf16x8*>(
+                        &k_lane[buf * kKTileElems + kb * 32 * kKStride + ks * 16]);
                     s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, qf[ks], s[kb], 0, 0, 0);
                 }
 
@@ -300,7 +305,7 @@ __device__ __forceinline__ void attention_body(const AttnArgs& a, bf16_t* k_lds,
 #pragma unroll
                     for (int db = 0; db < kDv / 32; ++db) {
                         const bf16x8 af = *reinterpret_cast<const bf16x8*>(
-                            &vl[(db * 32 + l32) * kVtStride + g * 8 + kb * 32 + hh * 16]);
+                            &v_lane[buf * kVtTileElems + db * 32 * kVtStride + kb * 32 + hh * 16]);
                         o_acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, pb[kb][hh], o_acc[db], 0, 0, 0);
                     }
         }
@@ -308,6 +313,10 @@ __device__ __forceinline__ void attention_body(const AttnArgs& a, bf16_t* k_lds,
         // the other buffer was last read before the previous barrier
         if (t + 1 < n_tiles) store_tile(buf ^ 1);
         __syncthreads();
+    };
+    for (int32_t t = 0; t < n_tiles; t += 2) {
+        step(t, std::integral_constant<int, 0>{});
+        if (t + 1 < n_tiles) step(t + 1, std::integral_constant<int, 1>{});
     }
 
     // ---- epilogue: normalise, write bf16 output rows and the LSE

@@ -58,12 +58,12 @@ constexpr int kThreads = kWaves * 64;
 constexpr int kQPerWave = 32;
 constexpr int kBlockM = kWaves * kQPerWave;  // queries per workgroup
 constexpr int kBlockN = 64;                  // keys per tile
-constexpr int kKStride = kDk + 8;            // K tile LDS row stride (elements): 400 B
+constexpr int kKRowBytes = kDk * 2;         // K tile LDS row: 384 B, 24 chunks of 16 B, unpadded
 constexpr int kVtStride = kBlockN + 8;       // V^T tile LDS row stride (elements): 144 B
 constexpr int kKVecPerRow = kDk / 8;         // 24 16-byte vectors per K row
-constexpr int kKLoads = kBlockN * kKVecPerRow / kThreads;  // 3 per thread
+constexpr int kKLoads = kBlockN * kKVecPerRow / kThreads;  // 3 direct-to-LDS loads per lane
 constexpr int kVLoads = 2;                                  // 2 keys x 8 dims per thread
-constexpr int kKTileElems = kBlockN * kKStride;
+constexpr int kKTileBytes = kBlockN * kKRowBytes;  // 24 KB
 constexpr int kVtTileElems = kDv * kVtStride;
 constexpr float kRescaleThreshold = 8.0f;  // log2 units
 constexpr int kBufferConfig = 0x00020000;  // dword 3 of a raw buffer descriptor on gfx9
@@ -117,7 +117,7 @@ __device__ __forceinline__ int32_t xcd_logical_tile(int32_t bid, int32_t total) 
 }
 
 template <bool kCausal>
-__device__ __forceinline__ void attention_body(const AttnArgs& a, bf16_t* k_lds, bf16_t* vt_lds) {
+__device__ __forceinline__ void attention_body(const AttnArgs& a, unsigned char* k_lds, bf16_t* vt_lds) {
     const int32_t tile = xcd_logical_tile(blockIdx.x, a.total_tiles);
     int32_t qt = tile % a.q_tiles;
     const int32_t rest = tile / a.q_tiles;
@@ -167,40 +167,48 @@ __device__ __forceinline__ void attention_body(const AttnArgs& a, bf16_t* k_lds,
     const bf16_t* vseq = a.v + static_cast<int64_t>(k_begin) * H * kDv + static_cast<int64_t>(head) * kDv;
     const int32_t k_row_bytes = H * kDk * 2;
     const int32_t v_row_bytes = H * kDv * 2;
-    int32_t k_goff[kKLoads], k_loff[kKLoads];
+    // K tile in LDS: row r (key) holds its 24 16-byte chunks with chunk c at
+    // position c ^ (r & 7), so that the 32 rows read by one MFMA operand load
+    // hit distinct banks without padding.  Each wave fills 3 KB of the tile
+    // with direct-to-LDS loads (lane l writes 16 bytes at l * 16); the lane
+    // picks the global chunk that belongs at that LDS position.
+    int32_t k_goff[kKLoads];
 #pragma unroll
     for (int i = 0; i < kKLoads; ++i) {
-        const int vidx = tid + i * kThreads;
-        const int key = vidx / kKVecPerRow;
-        const int c = vidx - key * kKVecPerRow;
-        k_goff[i] = key * k_row_bytes + c * 16;
-        k_loff[i] = key * kKStride + c * 8;
+        const int pbyte = (wave * kKLoads + i) * 1024 + lane * 16;
+        const int row = pbyte / kKRowBytes;
+        const int chunk = ((pbyte % kKRowBytes) >> 4) ^ (row & 7);
+        k_goff[i] = row * k_row_bytes + chunk * 16;
     }
     const int vkp = tid & 31;  // keys 2*vkp, 2*vkp+1 of the tile
     const int vdc = tid >> 5;  // dims 8*vdc .. 8*vdc+7
     const int32_t v_goff = 2 * vkp * v_row_bytes + vdc * 16;
     const int v_lpos = vt_pos(2 * vkp);
 
-    u32x4 kreg[kKLoads];
     u32x4 vreg[kVLoads];
-    auto load_tile = [&](int32_t k0) {
+    // K(k0 tile) straight into K buffer `buf` (no registers involved)
+    auto load_k = [&](int32_t k0, int buf) {
         const int32_t keys = min(kBlockN, kv_end - k0);
         const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
             const_cast<bf16_t*>(kseq + static_cast<int64_t>(k0) * H * kDk), 0, keys * k_row_bytes, kBufferConfig);
+        unsigned char* dst = k_lds + buf * kKTileBytes + wave * kKLoads * 1024;
+#pragma unroll
+        for (int i = 0; i < kKLoads; ++i)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rk, (__attribute__((address_space(3))) void*)(dst + i * 1024), 16, k_goff[i], 0, 0,
+                0);
+    };
+    auto load_v = [&](int32_t k0) {
+        const int32_t keys = min(kBlockN, kv_end - k0);
         const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
             const_cast<bf16_t*>(vseq + static_cast<int64_t>(k0) * H * kDv), 0, keys * v_row_bytes, kBufferConfig);
-#pragma unroll
-        for (int i = 0; i < kKLoads; ++i) kreg[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, k_goff[i], 0, 0);
 #pragma unroll
         for (int u = 0; u < kVLoads; ++u)
             vreg[u] = __builtin_amdgcn_raw_buffer_load_b128(rv, v_goff + u * v_row_bytes, 0, 0);
     };
-    auto store_tile = [&](int buf) {
-        bf16_t* kl = k_lds + buf * kKTileElems;
-        bf16_t* vl = vt_lds + buf * kVtTileElems;
-#pragma unroll
-        for (int i = 0; i < kKLoads; ++i) *reinterpret_cast<u32x4*>(&kl[k_loff[i]]) = kreg[i];
+    auto store_v = [&](int buf) {
         // transpose 2 keys x 8 dims into 8 rows (dims) of 2 keys
+        bf16_t* vl = vt_lds + buf * kVtTileElems;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const uint32_t w0 = vreg[0][i], w1 = vreg[1][i];
@@ -211,112 +219,163 @@ __device__ __forceinline__ void attention_body(const AttnArgs& a, bf16_t* k_lds,
     };
 
     const int32_t n_tiles = (kv_end + kBlockN - 1) / kBlockN;
-    const int32_t wave_last_q = qt * kBlockM + wave * kQPerWave + kQPerWave - 1;
+    const int32_t wave_first_q = qt * kBlockM + wave * kQPerWave;
+    const int32_t wave_last_q = wave_first_q + kQPerWave - 1;
     // per-lane LDS bases; every fragment read is base + a compile-time offset
-    const bf16_t* k_lane = k_lds + l32 * kKStride + g * 8;
+    // per-lane K fragment addresses for the four values of ks & 3
+    // (chunk 2*ks + g sits at (2*ks + g) ^ (l32 & 7) in row kb*32 + l32)
+    const unsigned char* k_lane[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) k_lane[m] = k_lds + l32 * kKRowBytes + (((2 * m + g) ^ (l32 & 7)) << 4);
     const bf16_t* v_lane = vt_lds + l32 * kVtStride + g * 8;
+
+    // S^T = K Q^T of one tile, from K buffer `kbuf` (compile-time)
+    auto qk = [&](f32x16 (&s)[2], auto kbuf_tag) {
+        constexpr int kbuf = decltype(kbuf_tag)::value;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < kDk / 16; ++ks)
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+                const bf16x8 af = *reinterpret_cast<const bf16x8*>(
+                    k_lane[ks & 3] + kbuf * kKTileBytes + kb * 32 * kKRowBytes + (ks >> 2) * 128);
+                s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, qf[ks], s[kb], 0, 0, 0);
+            }
+        // schedule: 8 fragment reads ahead, then alternate MFMA / read
+        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+    };
+
+    // Software pipeline over key tiles.  Tile j's scores S(j) are computed one
+    // iteration ahead: iteration j does the softmax of S(j) interleaved with
+    // O += V(j) P(j) (each P fragment is produced just before the MFMAs that
+    // consume it), then issues the MFMAs of S(j+1), whose results are only
+    // needed after the barrier.
+    // LDS: K runs one tile ahead of V, each in a ring of two buffers; at the
+    // end of iteration j, K(j+2) overwrites K(j) (last read in iteration j-1)
+    // and V(j+1) overwrites V(j-1) (also last read in iteration j-1), then one
+    // barrier publishes them.
+    f32x16 s_cur[2], s_nxt[2];
     if (n_tiles > 0) {
-        load_tile(0);
-        store_tile(0);
+        load_k(0, 0);
+        if (n_tiles > 1) load_k(kBlockN, 1);
+        load_v(0);
+        store_v(0);
     }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // direct-to-LDS loads have landed
     __syncthreads();
+    if (n_tiles > 0 && (!kCausal || 0 <= wave_last_q)) qk(s_cur, std::integral_constant<int, 0>{});
+    __syncthreads();  // K(0) is overwritten by K(2) at the end of iteration 0
 
-    // one key tile: compute on LDS buffer `buf` (a compile-time constant so
-    // that the LDS reads use immediate offsets), stage the next tile into the
-    // other buffer, barrier
-    auto step = [&](int32_t t, auto buf_tag) {
-        constexpr int buf = decltype(buf_tag)::value;
-        const int32_t k0 = t * kBlockN;
-        if (t + 1 < n_tiles) load_tile(k0 + kBlockN);
+    auto step = [&](int32_t j, auto par_tag) {
+        constexpr int par = decltype(par_tag)::value;  // j & 1
+        const int32_t k0 = j * kBlockN;
+        // K(j+2) goes straight into the buffer that held K(j), last read in
+        // iteration j-1 (before the previous barrier)
+        if (j + 2 < n_tiles) load_k(k0 + 2 * kBlockN, par);
+        if (j + 1 < n_tiles) load_v(k0 + kBlockN);
+        const bool active = !kCausal || k0 <= wave_last_q;  // a causal wave past this tile skips it
 
-        // a causal wave whose queries all precede this tile has nothing to do
-        if (!kCausal || k0 <= wave_last_q) {
-            // ---- S^T = K Q^T for two 32-key blocks
-            f32x16 s[2];
+        // ---- mask keys of S(j) past the end (and above the diagonal when causal)
+        if (active && ((k0 + kBlockN > kv_end) || (kCausal && k0 + kBlockN - 1 > wave_first_q))) {
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
-#pragma unroll
-            for (int ks = 0; ks < kDk / 16; ++ks)
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb) {
-                    const bf16x8 af = *reinterpret_cast<const bf16x8*>(
-                        &k_lane[buf * kKTileElems + kb * 32 * kKStride + ks * 16]);
-                    s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, qf[ks], s[kb], 0, 0, 0);
+                for (int r = 0; r < 16; ++r) {
+                    const int32_t key = k0 + kb * 32 + (r >> 2) * 8 + g * 4 + (r & 3);
+                    const bool dead = key >= kv_end || (kCausal && key > q_row);
+                    if (dead) s_cur[kb][r] = -INFINITY;
                 }
+        }
 
-            // ---- mask keys past the end (and above the diagonal when causal)
-            const bool need_mask = (k0 + kBlockN > kv_end) ||
-                                   (kCausal && k0 + kBlockN - 1 > qt * kBlockM + wave * kQPerWave);
-            if (need_mask) {
+        auto scores_next = [&]() {
+            // ---- MFMAs of S(j+1).  Non-causal: issued unconditionally, so
+            // that they share a basic block with the neighbouring VALU work;
+            // on the last tile they read the other K buffer's stale (in-bounds)
+            // contents and the result is never used.
+            if (kCausal) {
+                if (j + 1 < n_tiles && k0 + kBlockN <= wave_last_q)
+                    qk(s_nxt, std::integral_constant<int, par ^ 1>{});
+            } else {
+                qk(s_nxt, std::integral_constant<int, par ^ 1>{});
+            }
+        };
+        auto softmax_pv = [&]() {
+            if (active) {
+                // ---- online softmax of S(j) (base 2), lazily raised reference max
+                float mx = -INFINITY;
 #pragma unroll
                 for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int32_t key = k0 + kb * 32 + (r >> 2) * 8 + g * 4 + (r & 3);
-                        const bool dead = key >= kv_end || (kCausal && key > q_row);
-                        if (dead) s[kb][r] = -INFINITY;
-                    }
-            }
-
-            // ---- online softmax (base 2) with a lazily raised reference max
-            float mx = -INFINITY;
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-            const float m_tile = pair_max(mx) * a.scale_log2;
-            const bool raise = m_tile > m_run + kRescaleThreshold;
-            if (__builtin_amdgcn_ballot_w64(raise) != 0) {
+                    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s_cur[kb][r]);
+                const float m_tile = pair_max(mx) * a.scale_log2;
+                const bool raise = m_tile > m_run + kRescaleThreshold;
+                const bool any_raise = __builtin_amdgcn_ballot_w64(raise) != 0;
                 const float m_new = raise ? m_tile : m_run;
-                const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 0 when m_run is -inf
-                l_run *= alpha;
-#pragma unroll
-                for (int db = 0; db < kDv / 32; ++db)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) o_acc[db][r] *= alpha;
+                const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 1 if kept, 0 if m_run was -inf
                 m_run = m_new;
-            }
-            const float m_use = m_run == -INFINITY ? 0.f : m_run;
-            bf16x8 pb[2][2];
+                const float m_use = m_new == -INFINITY ? 0.f : m_new;
+                float psum = 0.f;
+                bf16x8 pb[2][2];
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
+                for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-                for (int hh = 0; hh < 2; ++hh) {
-                    uint32_t pk[4];
+                    for (int hh = 0; hh < 2; ++hh) {
+                        uint32_t pk[4];
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        const float p0 =
-                            __builtin_amdgcn_exp2f(fmaf(s[kb][hh * 8 + 2 * j], a.scale_log2, -m_use));
-                        const float p1 =
-                            __builtin_amdgcn_exp2f(fmaf(s[kb][hh * 8 + 2 * j + 1], a.scale_log2, -m_use));
-                        l_run += p0 + p1;
-                        pk[j] = pack_bf16x2(p0, p1);
+                        for (int jj = 0; jj < 4; ++jj) {
+                            const float p0 =
+                                __builtin_amdgcn_exp2f(fmaf(s_cur[kb][hh * 8 + 2 * jj], a.scale_log2, -m_use));
+                            const float p1 =
+                                __builtin_amdgcn_exp2f(fmaf(s_cur[kb][hh * 8 + 2 * jj + 1], a.scale_log2, -m_use));
+                            psum += p0 + p1;
+                            pk[jj] = pack_bf16x2(p0, p1);
+                        }
+                        pb[kb][hh] = __builtin_bit_cast(bf16x8, make_uint4(pk[0], pk[1], pk[2], pk[3]));
                     }
-                    pb[kb][hh] = __builtin_bit_cast(bf16x8, make_uint4(pk[0], pk[1], pk[2], pk[3]));
+                l_run = l_run * alpha + psum;
+                if (any_raise) {
+#pragma unroll
+                    for (int db = 0; db < kDv / 32; ++db)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) o_acc[db][r] *= alpha;
                 }
 
-            // ---- O^T += V^T P^T (4 independent accumulator chains)
+                // ---- O^T += V(j)^T P(j)^T (4 independent accumulator chains)
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
+                for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-                for (int hh = 0; hh < 2; ++hh)
+                    for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
-                    for (int db = 0; db < kDv / 32; ++db) {
-                        const bf16x8 af = *reinterpret_cast<const bf16x8*>(
-                            &v_lane[buf * kVtTileElems + db * 32 * kVtStride + kb * 32 + hh * 16]);
-                        o_acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, pb[kb][hh], o_acc[db], 0, 0, 0);
-                    }
-        }
+                        for (int db = 0; db < kDv / 32; ++db) {
+                            const bf16x8 af = *reinterpret_cast<const bf16x8*>(
+                                &v_lane[par * kVtTileElems + db * 32 * kVtStride + kb * 32 + hh * 16]);
+                            o_acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, pb[kb][hh], o_acc[db], 0, 0, 0);
+                        }
+            }
+        };
+        // softmax and O update of tile j first; the MFMAs of S(j+1) then run
+        // while the wave moves on to the end-of-tile wait and barrier
+        softmax_pv();
+        if (j + 1 < n_tiles) store_v(par ^ 1);  // V(j-1)'s buffer: last read in iteration j-1
+        scores_next();
 
-        // the other buffer was last read before the previous barrier
-        if (t + 1 < n_tiles) store_tile(buf ^ 1);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // K(j+2) has landed in LDS
         __syncthreads();
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) s_cur[kb] = s_nxt[kb];
     };
-    for (int32_t t = 0; t < n_tiles; t += 2) {
-        step(t, std::integral_constant<int, 0>{});
-        if (t + 1 < n_tiles) step(t + 1, std::integral_constant<int, 1>{});
+    for (int32_t j = 0; j < n_tiles; j += 2) {
+        step(j, std::integral_constant<int, 0>{});
+        if (j + 1 < n_tiles) step(j + 1, std::integral_constant<int, 1>{});
     }
 
     // ---- epilogue: normalise, write bf16 output rows and the LSE
@@ -340,13 +399,13 @@ __device__ __forceinline__ void attention_body(const AttnArgs& a, bf16_t* k_lds,
 
 // Distinct entry points so that profiles separate the two steps.
 __global__ __launch_bounds__(kThreads, 1) void chunk_attention_kernel(AttnArgs a) {
-    __shared__ __attribute__((aligned(16))) bf16_t k_lds[2 * kKTileElems];
+    __shared__ __attribute__((aligned(1024))) unsigned char k_lds[2 * kKTileBytes];
     __shared__ __attribute__((aligned(16))) bf16_t vt_lds[2 * kVtTileElems];
     attention_body<false>(a, k_lds, vt_lds);
 }
 
 __global__ __launch_bounds__(kThreads, 1) void suffix_attention_kernel(AttnArgs a) {
-    __shared__ __attribute__((aligned(16))) bf16_t k_lds[2 * kKTileElems];
+    __shared__ __attribute__((aligned(1024))) unsigned char k_lds[2 * kKTileBytes];
     __shared__ __attribute__((aligned(16))) bf16_t vt_lds[2 * kVtTileElems];
     attention_body<true>(a, k_lds, vt_lds);
 }

@@ -22,6 +22,14 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     return __builtin_bit_cast(uint32_t, v);
 }
 
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+
+// 16-byte load with a non-temporal hint (data read once)
+__device__ __forceinline__ uint4 load_nt(const uint4* p) {
+    const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+    return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
 // ---------------------------------------------------------------- init
 
 __global__ __launch_bounds__(kThreads) void init_partial_kernel(uint4* out, float* lse, int64_t lse_stride,
@@ -54,47 +62,55 @@ struct MergeArgs {
     int64_t prefix_num_tokens;
 };
 
-// Merge of one 8-element vector of one (token, head) row.  The prefix side is
-// not read at or past the threshold, and the side of an empty state (LSE -inf)
-// is never read: the result is selected, not multiplied by zero.
+// Merge of one 8-element vector of one (token, head) row, given both rows'
+// vectors and LSEs.  An empty side (LSE -inf) is never used: the result is
+// selected, not multiplied by zero, so NaN or garbage in it cannot leak.
+__device__ __forceinline__ uint4 merge_values(float pl, float sl, const uint4& pv, const uint4& sv, float& ol) {
+    const bool pe = pl == -INFINITY, se = sl == -INFINITY;
+    if (pe && se) {
+        ol = -INFINITY;
+        return make_uint4(0u, 0u, 0u, 0u);
+    }
+    if (pe) {
+        ol = sl;
+        return sv;
+    }
+    if (se) {
+        ol = pl;
+        return pv;
+    }
+    const float m = fmaxf(pl, sl);
+    const float wp = expf(pl - m), ws = expf(sl - m);
+    const float tot = wp + ws;
+    const float fp = wp / tot, fs = ws / tot;
+    const uint32_t pw[4] = {pv.x, pv.y, pv.z, pv.w};
+    const uint32_t sw[4] = {sv.x, sv.y, sv.z, sv.w};
+    uint32_t rw[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const float lo = fp * bf16_to_f32(pw[k] & 0xffffu) + fs * bf16_to_f32(sw[k] & 0xffffu);
+        const float hi = fp * bf16_to_f32(pw[k] >> 16) + fs * bf16_to_f32(sw[k] >> 16);
+        rw[k] = pack_bf16x2(lo, hi);
+    }
+    ol = m + logf(tot);
+    return make_uint4(rw[0], rw[1], rw[2], rw[3]);
+}
+
+// One vector of one row, for the generic kernel.  The prefix side is not
+// read at or past the threshold.
 __device__ __forceinline__ void merge_vec(const MergeArgs& a, int64_t t, int32_t h, int64_t vec_index,
                                           bool write_lse) {
     const float sl = a.s_lse[h * a.s_stride + t];
+    const uint4 sv = a.s_out[vec_index];
     float ol;
     uint4 res;
     if (t >= a.prefix_num_tokens) {
-        res = a.s_out[vec_index];
+        res = sv;
         ol = sl;
     } else {
         const float pl = a.p_lse[h * a.p_stride + t];
-        const bool pe = pl == -INFINITY, se = sl == -INFINITY;
-        if (pe && se) {
-            res = make_uint4(0u, 0u, 0u, 0u);
-            ol = -INFINITY;
-        } else if (pe) {
-            res = a.s_out[vec_index];
-            ol = sl;
-        } else if (se) {
-            res = a.p_out[vec_index];
-            ol = pl;
-        } else {
-            const float m = fmaxf(pl, sl);
-            const float wp = expf(pl - m), ws = expf(sl - m);
-            const float tot = wp + ws;
-            const float fp = wp / tot, fs = ws / tot;
-            const uint4 pv = a.p_out[vec_index], sv = a.s_out[vec_index];
-            const uint32_t pw[4] = {pv.x, pv.y, pv.z, pv.w};
-            const uint32_t sw[4] = {sv.x, sv.y, sv.z, sv.w};
-            uint32_t rw[4];
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const float lo = fp * bf16_to_f32(pw[k] & 0xffffu) + fs * bf16_to_f32(sw[k] & 0xffffu);
-                const float hi = fp * bf16_to_f32(pw[k] >> 16) + fs * bf16_to_f32(sw[k] >> 16);
-                rw[k] = pack_bf16x2(lo, hi);
-            }
-            res = make_uint4(rw[0], rw[1], rw[2], rw[3]);
-            ol = m + logf(tot);
-        }
+        const uint4 pv = a.p_out[vec_index];
+        res = merge_values(pl, sl, pv, sv, ol);
     }
     a.out[vec_index] = res;
     if (write_lse && a.out_lse != nullptr) a.out_lse[h * a.out_stride + t] = ol;
@@ -102,7 +118,8 @@ __device__ __forceinline__ void merge_vec(const MergeArgs& a, int64_t t, int32_t
 
 // head_dim 128: a block covers 16 consecutive tokens x 4 heads; 16 lanes per
 // (token, head) row of 256 bytes.  Consecutive tokens of one head share the
-// LSE cache lines.
+// LSE cache lines.  All loads of a lane are issued before any result is
+// formed, so that 8 row vectors are in flight per lane.
 constexpr int kMergeTokens = 16;
 constexpr int kMergeHeads = 4;
 
@@ -111,11 +128,31 @@ __global__ __launch_bounds__(kThreads) void merge_kernel_d128(MergeArgs a) {
     const int64_t t = static_cast<int64_t>(blockIdx.x) * kMergeTokens + (threadIdx.x >> 4);
     if (t >= a.tokens) return;
     const int32_t h0 = blockIdx.y * kMergeHeads;
+    const int nh = min(kMergeHeads, a.heads - h0);
+    const bool has_prefix = t < a.prefix_num_tokens;
+    uint4 pv[kMergeHeads], sv[kMergeHeads];
+    float pl[kMergeHeads], sl[kMergeHeads];
 #pragma unroll
     for (int hh = 0; hh < kMergeHeads; ++hh) {
-        const int32_t h = h0 + hh;
-        if (h >= a.heads) break;
-        merge_vec(a, t, h, (t * a.heads + h) * 16 + lane_vec, lane_vec == 0);
+        if (hh < nh) {
+            const int64_t vi = (t * a.heads + h0 + hh) * 16 + lane_vec;
+            sv[hh] = load_nt(&a.s_out[vi]);
+            sl[hh] = a.s_lse[(h0 + hh) * a.s_stride + t];
+            if (has_prefix) {
+                pv[hh] = load_nt(&a.p_out[vi]);
+                pl[hh] = a.p_lse[(h0 + hh) * a.p_stride + t];
+            }
+        }
+    }
+#pragma unroll
+    for (int hh = 0; hh < kMergeHeads; ++hh) {
+        if (hh < nh) {
+            const int32_t h = h0 + hh;
+            float ol = sl[hh];
+            const uint4 res = has_prefix ? merge_values(pl[hh], sl[hh], pv[hh], sv[hh], ol) : sv[hh];
+            a.out[(t * a.heads + h) * 16 + lane_vec] = res;
+            if (lane_vec == 0 && a.out_lse != nullptr) a.out_lse[h * a.out_stride + t] = ol;
+        }
     }
 }
 
@@ -134,23 +171,36 @@ __global__ __launch_bounds__(kThreads) void merge_kernel_generic(MergeArgs a) {
 
 // ---------------------------------------------------------------- gather
 
-constexpr int kGatherRows = 4;    // workspace rows per block
-constexpr int kGatherUnroll = 4;  // 16-byte vectors in flight per lane per pass
+constexpr int kGatherRows = 4;   // workspace rows per block
+constexpr int kGatherBatch = 8;  // 16-byte vectors in flight per lane (K and V of a row together)
 
-__device__ __forceinline__ void copy_row(const uint4* __restrict__ src, uint4* __restrict__ dst, int n,
+// Copy of one workspace row (its K vectors, then its V vectors, as one
+// sequence of kvec + vvec 16-byte vectors): every lane issues up to
+// kGatherBatch loads before its stores.  The cache is read once: non-temporal
+// loads keep it from displacing lines that are reused.
+__device__ __forceinline__ void copy_row(const uint4* __restrict__ ksrc, const uint4* __restrict__ vsrc,
+                                         uint4* __restrict__ kdst, uint4* __restrict__ vdst, int kvec, int vvec,
                                          bool ok) {
     const uint4 nan4 = make_uint4(0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u);
-    for (int base = threadIdx.x; base < n; base += kThreads * kGatherUnroll) {
-        uint4 r[kGatherUnroll];
+    const int n = kvec + vvec;
+    for (int base = threadIdx.x; base < n; base += kThreads * kGatherBatch) {
+        uint4 r[kGatherBatch];
 #pragma unroll
-        for (int u = 0; u < kGatherUnroll; ++u) {
+        for (int u = 0; u < kGatherBatch; ++u) {
             const int v = base + u * kThreads;
-            r[u] = (ok && v < n) ? src[v] : nan4;
+            r[u] = nan4;
+            if (ok && v < n) r[u] = v < kvec ? load_nt(&ksrc[v]) : load_nt(&vsrc[v - kvec]);
         }
 #pragma unroll
-        for (int u = 0; u < kGatherUnroll; ++u) {
+        for (int u = 0; u < kGatherBatch; ++u) {
             const int v = base + u * kThreads;
-            if (v < n) dst[v] = r[u];
+            if (v < n) {
+                const u32x4_t val = {r[u].x, r[u].y, r[u].z, r[u].w};
+                if (v < kvec)
+                    __builtin_nontemporal_store(val, reinterpret_cast<u32x4_t*>(&kdst[v]));
+                else
+                    __builtin_nontemporal_store(val, reinterpret_cast<u32x4_t*>(&vdst[v - kvec]));
+            }
         }
     }
 }
@@ -183,8 +233,8 @@ __global__ __launch_bounds__(kThreads) void gather_kernel(
         ok = ok && blk >= 0 && blk < num_blocks;
         if (!ok) blk = 0;
         const int64_t src_row = blk * block_size + slot;
-        copy_row(k_cache + src_row * kvec, ws_k + static_cast<int64_t>(w) * kvec, kvec, ok);
-        copy_row(v_cache + src_row * vvec, ws_v + static_cast<int64_t>(w) * vvec, vvec, ok);
+        copy_row(k_cache + src_row * kvec, v_cache + src_row * vvec, ws_k + static_cast<int64_t>(w) * kvec,
+                 ws_v + static_cast<int64_t>(w) * vvec, kvec, vvec, ok);
     }
 }
 

@@ -47,9 +47,34 @@ def work_figures(wl, chunks):
     final_merge_bytes = T * H * merge_row
     cont_rows = sum(ql[c["request_begin"]] for c in chunks if c["is_continuation"])
     accumulate_bytes = cont_rows * H * merge_row
-    return dict(chunk_flops=chunk_flops, suffix_flops=suffix_flops, gather_bytes=gather_bytes,
+    # chunk attention must read Q, the gathered K/V rows and write O + LSE
+    q_rows = sum(sum(ql[c["request_begin"]:c["request_end"]]) for c in chunks)
+    chunk_bytes = H * (q_rows * (192 * 2 + 128 * 2 + 4) + rows * (192 + 128) * 2)
+    return dict(chunk_flops=chunk_flops, suffix_flops=suffix_flops, gather_bytes=gather_bytes, chunk_bytes=chunk_bytes,
                 merge_bytes=final_merge_bytes + accumulate_bytes, final_merge_bytes=final_merge_bytes,
                 accumulate_bytes=accumulate_bytes)
+
+
+def profiled_traffic(kernel, workload):
+    """HBM bytes per launch of `kernel` from the committed counter profile, if
+    it was taken on this workload and the kernel's sources are unchanged since
+    (else None)."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"{workload}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        prof = json.load(f)
+    k = prof.get("kernels", {}).get(kernel)
+    if k is None:
+        return None
+    h = hashlib.sha256()
+    for src in k["sources"]:
+        with open(os.path.join(ROOT, src), "rb") as f:
+            h.update(f.read())
+    if h.hexdigest() != k["source_sha256"]:
+        return None
+    return k["fetch_bytes_per_launch"] + k["write_bytes_per_launch"]
 
 
 def cpu_baseline(b, wl, sample_queries):
@@ -176,7 +201,10 @@ def main():
         "roofline": {"kernel": "chunk_attn", "bound": "mfma",
                      "achieved": round(ca_tflops, 2) if ca_tflops else None, "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(ca_tflops / PEAK_BF16_TFLOPS, 4) if ca_tflops else None,
-                     "traffic": None, "launches_per_step": n_ca / K,
+                     "traffic": profiled_traffic("chunk_attention_kernel", wl.name),
+                     "traffic_unit": "bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
+                     "algorithmic_bytes_per_launch": (wf["chunk_bytes"] / n_ca * K) if n_ca else None,
+                     "launches_per_step": n_ca / K,
                      "flops_per_launch": wf["chunk_flops"] * K / n_ca if n_ca else None,
                      "avg_launch_ms": round(ms_ca / n_ca, 4) if n_ca else None},
         "kernels": kernels,

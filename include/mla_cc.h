@@ -202,6 +202,27 @@ int mla_merge_attn_states(void* out, float* out_lse, const void* prefix_out, con
                           int64_t prefix_lse_stride, int64_t suffix_lse_stride,
                           int64_t prefix_num_tokens, void* stream);
 
+/*
+ * mask_empty_context (PR #49294 digest, 实现拆解 items 1-2; test_mask_empty_context
+ * in 关键源码片段), in place: for every request r whose context in this chunk
+ * is empty (context_start_loc[r+1] == context_start_loc[r]), set the LSE of
+ * its query rows query_start_loc[r] .. query_start_loc[r+1]-1 to -inf for all
+ * heads and zero those output rows; every other row is left untouched.  Each
+ * row's request is found by a wavefront-parallel search over query_start_loc
+ * (no per-token metadata).  The chunked prefill above initialises the context
+ * partial instead (PR #50613 digest, 实现拆解 item 3); this is the earlier
+ * mechanism, kept as an operation of its own.
+ *   lse                dev fp32 [H, lse_head_stride >= num_tokens]
+ *   output             dev [num_tokens, H, head_dim], elements of elem_bytes (2: bf16, 4: fp32),
+ *                      4-byte aligned, head_dim * elem_bytes a multiple of 4
+ *   query_start_loc    dev int32 [num_requests + 1], nondecreasing from 0
+ *   context_start_loc  dev int32 [num_requests + 1]
+ */
+int mla_mask_empty_context(float* lse, int64_t lse_head_stride, void* output, int32_t elem_bytes,
+                           const int32_t* query_start_loc, const int32_t* context_start_loc,
+                           int32_t num_requests, int64_t num_tokens, int32_t num_heads, int32_t head_dim,
+                           void* stream);
+
 /* Inputs, outputs and scratch of one chunked prefill (all dev pointers are
  * caller-owned; lens are host arrays). */
 typedef struct mla_chunked_prefill_params {
@@ -263,7 +284,8 @@ enum {
     MLA_KERNEL_CHUNK_ATTN = 2,
     MLA_KERNEL_SUFFIX_ATTN = 3,
     MLA_KERNEL_MERGE = 4,
-    MLA_KERNEL_KINDS = 5
+    MLA_KERNEL_MASK = 5,
+    MLA_KERNEL_KINDS = 6
 };
 
 typedef struct mla_kernel_time {

@@ -54,7 +54,10 @@ class ChunkedPrefillParams(ctypes.Structure):
 
 
 def _sig(name, *argtypes):
-    f = getattr(_lib, name)
+    try:
+        f = getattr(_lib, name)
+    except AttributeError as e:
+        raise ImportError(f"{LIB_PATH} does not export {name}: it is stale, rebuild it") from e
     f.argtypes = list(argtypes)
     f.restype = ctypes.c_int
     return f
@@ -76,6 +79,7 @@ _suffix_attn = _sig("mla_causal_suffix_attn", _ptr, _ptr, _ptr, _ptr, _i32, _i32
                     _ptr, _i64, _ptr)
 _merge = _sig("mla_merge_attn_states", _ptr, _ptr, _ptr, _ptr, _ptr, _ptr, _i64, _i32, _i32, _i64, _i64, _i64,
               _i64, _ptr)
+_mask = _sig("mla_mask_empty_context", _ptr, _i64, _ptr, _i32, _ptr, _ptr, _i32, _i64, _i32, _i32, _ptr)
 _scratch_size = _sig("mla_chunked_prefill_scratch_size", ctypes.POINTER(ChunkedPrefillParams), _i64p)
 _prefill = _sig("mla_chunked_prefill", ctypes.POINTER(ChunkedPrefillParams), _ptr)
 
@@ -83,7 +87,7 @@ class KernelTime(ctypes.Structure):
     _fields_ = [("launches", ctypes.c_int64), ("total_ms", ctypes.c_double)]
 
 
-KERNEL_KINDS = ["init", "gather", "chunk_attn", "suffix_attn", "merge"]
+KERNEL_KINDS = ["init", "gather", "chunk_attn", "suffix_attn", "merge", "mask"]
 _timing_enable = _sig("mla_kernel_timing_enable", ctypes.c_int)
 _timing_read = _sig("mla_kernel_timing_read", ctypes.POINTER(KernelTime))
 
@@ -91,7 +95,7 @@ EXPORTED = [
     "mla_status_string", "mla_abi_version", "mla_plan_context_chunks", "mla_prefill_token_info",
     "mla_init_context_partial", "mla_gather_context", "mla_context_chunk_attn", "mla_causal_suffix_attn",
     "mla_merge_attn_states", "mla_chunked_prefill_scratch_size", "mla_chunked_prefill",
-    "mla_kernel_timing_enable", "mla_kernel_timing_read",
+    "mla_kernel_timing_enable", "mla_kernel_timing_read", "mla_mask_empty_context",
 ]
 
 
@@ -214,6 +218,14 @@ def mla_merge_attn_states(out, out_lse, prefix_out, prefix_lse, suffix_out, suff
                   _dptr(suffix_lse), T, H, D, out_lse.shape[1] if out_lse is not None else 0,
                   prefix_lse.shape[1] if prefix_lse is not None else 0, suffix_lse.shape[1], pnt,
                   _stream(stream)), "mla_merge_attn_states")
+
+
+def mla_mask_empty_context(lse, output, query_start_loc, context_start_loc, stream=None):
+    """In place.  lse [H, stride] fp32; output [T, H, D] bf16 or fp32; start locs int32 [N+1] on device."""
+    T, H, D = output.shape
+    _check(_mask(_dptr(lse), lse.shape[1], _dptr(output), output.element_size(), _dptr(query_start_loc),
+                 _dptr(context_start_loc), query_start_loc.numel() - 1, T, H, D, _stream(stream)),
+           "mla_mask_empty_context")
 
 
 def make_prefill_params(q, k_new, v_new, k_cache, v_cache, block_table, context_lens, query_lens, workspace_rows,

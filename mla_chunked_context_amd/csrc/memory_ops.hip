@@ -238,6 +238,38 @@ __global__ __launch_bounds__(kThreads) void gather_kernel(
     }
 }
 
+// ---------------------------------------------------------------- mask
+
+// One wave per token row.  The row's request is found by a wavefront-parallel
+// search over query_start_loc: lanes load a window of 64 consecutive entries
+// and a ballot of (entry <= token) counts how many of them start at or before
+// it; the last such entry is the request (requests with no queries share a
+// start with their successor and are skipped by taking the last).  No
+// per-token metadata is needed.
+constexpr int kMaskWavesPerBlock = kThreads / 64;
+
+__global__ __launch_bounds__(kThreads) void mask_empty_context_kernel(
+    float* lse, int64_t lse_stride, uint32_t* out, int64_t row_words, const int32_t* __restrict__ qsl,
+    const int32_t* __restrict__ csl, int32_t num_requests, int64_t num_tokens, int32_t heads) {
+    const int lane = threadIdx.x & 63;
+    const int64_t t = static_cast<int64_t>(blockIdx.x) * kMaskWavesPerBlock + (threadIdx.x >> 6);
+    if (t >= num_tokens) return;
+    int32_t r = -1;
+    for (int32_t base = 0; base <= num_requests; base += 64) {
+        const int32_t idx = base + lane;
+        const bool le = idx <= num_requests && qsl[idx] <= t;
+        const uint64_t m = __builtin_amdgcn_ballot_w64(le);
+        const int cnt = __builtin_popcountll(m);
+        if (cnt > 0) r = base + cnt - 1;
+        if (cnt < 64) break;
+    }
+    if (r < 0 || r >= num_requests) return;  // a row past the last request is left alone
+    if (csl[r + 1] - csl[r] != 0) return;
+    for (int h = lane; h < heads; h += 64) lse[h * lse_stride + t] = -INFINITY;
+    uint32_t* row = out + t * row_words;
+    for (int64_t w = lane; w < row_words; w += 64) row[w] = 0u;
+}
+
 int grid_for(int64_t work, int64_t per_block, int64_t cap) {
     int64_t g = (work + per_block - 1) / per_block;
     if (g < 1) g = 1;
@@ -290,6 +322,18 @@ int launch_gather(const bf16_t* k_cache, const bf16_t* v_cache, int64_t num_bloc
                        reinterpret_cast<const uint4*>(k_cache), reinterpret_cast<const uint4*>(v_cache), num_blocks,
                        block_size, heads, block_table, bt_width, e_req, e_start, e_off, n_entries, num_rows,
                        reinterpret_cast<uint4*>(ws_k), reinterpret_cast<uint4*>(ws_v));
+    return hip_status(hipGetLastError());
+}
+
+int launch_mask_empty_context(float* lse, int64_t lse_stride, void* out, int32_t elem_bytes, const int32_t* qsl,
+                              const int32_t* csl, int32_t num_requests, int64_t num_tokens, int32_t heads,
+                              int32_t head_dim, hipStream_t stream) {
+    if (num_tokens <= 0) return MLA_OK;
+    const int64_t row_words = static_cast<int64_t>(heads) * head_dim * elem_bytes / 4;
+    const unsigned grid = static_cast<unsigned>((num_tokens + kMaskWavesPerBlock - 1) / kMaskWavesPerBlock);
+    TimedLaunch timed(MLA_KERNEL_MASK, stream);
+    hipLaunchKernelGGL(mask_empty_context_kernel, dim3(grid), dim3(kThreads), 0, stream, lse, lse_stride,
+                       static_cast<uint32_t*>(out), row_words, qsl, csl, num_requests, num_tokens, heads);
     return hip_status(hipGetLastError());
 }
 
@@ -353,3 +397,19 @@ int mla_gather_context(const void* k_cache, const void* v_cache, int64_t num_blo
 }
 
 }  // extern "C"
+
+extern "C" int mla_mask_empty_context(float* lse, int64_t lse_head_stride, void* output, int32_t elem_bytes,
+                                      const int32_t* query_start_loc, const int32_t* context_start_loc,
+                                      int32_t num_requests, int64_t num_tokens, int32_t num_heads, int32_t head_dim,
+                                      void* stream) {
+    if (num_requests < 0 || num_tokens < 0 || num_heads < 1 || head_dim < 1 || (elem_bytes != 2 && elem_bytes != 4))
+        return MLA_ERR_INVALID_ARG;
+    if ((static_cast<int64_t>(head_dim) * elem_bytes) % 4 != 0) return MLA_ERR_INVALID_ARG;
+    if (num_tokens == 0) return MLA_OK;
+    if (lse == nullptr || output == nullptr || query_start_loc == nullptr || context_start_loc == nullptr ||
+        lse_head_stride < num_tokens || (reinterpret_cast<uintptr_t>(output) & 3u) != 0)
+        return MLA_ERR_INVALID_ARG;
+    return mla::launch_mask_empty_context(lse, lse_head_stride, output, elem_bytes, query_start_loc,
+                                          context_start_loc, num_requests, num_tokens, num_heads, head_dim,
+                                          static_cast<hipStream_t>(stream));
+}

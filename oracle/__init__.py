@@ -20,6 +20,7 @@ Every floating-point step is float64.  Modules:
   attention  paged-cache gather and naive softmax attention with LSE
   merge      LSE merge, partial init/accumulate, thresholded final merge
   pipeline   the chunked prefill end to end, and the direct definition
+  mask       mask_empty_context (the earlier mechanism for empty rows)
 """
 from .planner import (ChunkPlan, ContextChunk, ChunkedContextMetadata, aligned_split_len,
                       plan_mla_context_chunks, build_mla_chunked_context_metadata,
@@ -28,11 +29,12 @@ from .attention import gather_context_rows, attention_with_lse
 from .merge import (merge_states, merge_attn_states, init_mla_context_partial,
                     accumulate_mla_context_chunk)
 from .pipeline import chunked_prefill, direct_prefill, direct_rows
+from .mask import mask_empty_context
 
 __all__ = [
     "ChunkPlan", "ContextChunk", "ChunkedContextMetadata", "aligned_split_len",
     "plan_mla_context_chunks", "build_mla_chunked_context_metadata", "build_chunked_context",
     "gather_context_rows", "attention_with_lse", "merge_states", "merge_attn_states",
     "init_mla_context_partial", "accumulate_mla_context_chunk", "chunked_prefill",
-    "direct_prefill", "direct_rows",
+    "direct_prefill", "direct_rows", "mask_empty_context",
 ]

@@ -165,3 +165,27 @@ def test_prefill_scratch_size_and_param_checks():
     p.split_alignment = 0
     with pytest.raises(mla.MlaError):
         mla.mla_chunked_prefill_scratch_size(p)
+
+
+def test_kernel_kinds_match_header():
+    text = open(os.path.join(ROOT, "include", "mla_cc.h")).read()
+    kinds = re.findall(r"MLA_KERNEL_([A-Z_]+) = (\d+)", text)
+    names = {int(v): k.lower() for k, v in kinds if k != "KINDS"}
+    assert len(mla.KERNEL_KINDS) == int(dict(kinds)["KINDS"])
+    assert [names[i] for i in range(len(names))] == list(mla.KERNEL_KINDS)
+
+
+def test_timing_read_without_launches():
+    mla.mla_kernel_timing_enable(True)
+    t = mla.mla_kernel_timing_read()
+    mla.mla_kernel_timing_enable(False)
+    assert all(v == (0, 0.0) for v in t.values())
+
+
+def test_mask_rejects_bad_arguments_without_gpu():
+    f = mla._lib
+    assert f.mla_mask_empty_context(ctypes.c_void_p(256), ctypes.c_int64(8), ctypes.c_void_p(256), 3,
+                                    ctypes.c_void_p(256), ctypes.c_void_p(256), 2, ctypes.c_int64(8), 2, 16,
+                                    None) == 1  # element size 3
+    assert f.mla_mask_empty_context(None, ctypes.c_int64(8), ctypes.c_void_p(256), 4, ctypes.c_void_p(256),
+                                    ctypes.c_void_p(256), 2, ctypes.c_int64(8), 2, 16, None) == 1

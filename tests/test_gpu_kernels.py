@@ -60,6 +60,7 @@ def test_merge_matches_oracle(head_dim, threshold):
     assert np.abs(l[fin] - ref_l[fin]).max() < 1e-5
     # copies and selects are bit-exact
     ob, pb, sb = _bits(out), _bits(po), _bits(so)
+    pl, sl = pl.numpy(), sl.numpy()
     k = T if threshold is None else threshold
     for t in range(T):
         for h in range(H):
@@ -248,3 +249,48 @@ def test_attention_is_deterministic():
     a = _varlen_case(21, [200, 33], [500, 70], 2, causal=False)
     b = _varlen_case(21, [200, 33], [500, 70], 2, causal=False)
     assert a == b
+
+
+# ------------------------------------------------------- mask_empty_context
+
+
+def _mask_case(query_lens, context_lens, H, D, dtype, seed, nan_rows=None):
+    qsl = np.concatenate([[0], np.cumsum(query_lens)]).astype(np.int32)
+    csl = np.concatenate([[0], np.cumsum(context_lens)]).astype(np.int32)
+    T = int(qsl[-1])
+    g = torch.Generator().manual_seed(seed)
+    lse = torch.randn(H, T, generator=g)
+    out = torch.randn(T, H, D, generator=g).to(dtype)
+    if nan_rows is not None:
+        out[nan_rows[0]:nan_rows[1]] = float("nan")
+    ref_l, ref_o = lse.double().numpy().copy(), out.double().numpy().copy()
+    O.mask_empty_context(ref_l, ref_o, qsl, csl)
+    dl, do = lse.to(DEV), out.to(DEV)
+    mla.mla_mask_empty_context(dl, do, torch.from_numpy(qsl).to(DEV), torch.from_numpy(csl).to(DEV))
+    torch.cuda.synchronize()
+    gl, go = dl.double().cpu().numpy(), do.double().cpu().numpy()
+    assert np.array_equal(gl, ref_l) and np.array_equal(np.isnan(go), np.isnan(ref_o))
+    assert np.array_equal(np.nan_to_num(go, nan=7.0), np.nan_to_num(ref_o, nan=7.0))
+    return gl, go
+
+
+def test_mask_empty_context_printed_test(golden):
+    """The PR #49294 digest's test: rows 33..163 (request 32, no context) end
+    (-inf, 0); every other value is untouched (fp32 outputs, as in the test)."""
+    g = golden("empty_context_rows.json")
+    say("mask_empty_context printed test")
+    e0, e1 = g["empty_rows"]
+    gl, go = _mask_case(g["query_lens"], g["context_lens"], g["num_heads"], g["head_dim"], torch.float32, 0,
+                        nan_rows=(e0, e1))
+    assert np.isneginf(gl[:, e0:e1]).all() and (go[e0:e1] == 0).all()
+    assert np.isfinite(gl[:, :e0]).all() and np.isfinite(gl[:, e1:]).all()
+
+
+@pytest.mark.parametrize("seed", [1, 2, 3])
+def test_mask_empty_context_random(seed):
+    rng = np.random.default_rng(seed)
+    n = int(rng.integers(60, 300))  # several 64-entry search windows
+    ql = [0 if rng.random() < 0.1 else int(rng.integers(1, 9)) for _ in range(n)]
+    cl = [0 if rng.random() < 0.3 else int(rng.integers(1, 50)) for _ in range(n)]
+    say(f"mask_empty_context random seed={seed} n={n}")
+    _mask_case(ql, cl, int(rng.integers(1, 9)), 128, torch.bfloat16, seed)

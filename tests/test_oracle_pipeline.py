@@ -167,3 +167,44 @@ def test_direct_rows_matches_direct_prefill():
     out, lse = O.direct_rows(f(b.q)[[4, 7]], [1, 4], np.stack(rows), np.stack(vrows), f(b.k_new)[3:8],
                              f(b.v_new)[3:8], wl.scale)
     assert np.allclose(out, d_out[[4, 7]], atol=1e-13) and np.allclose(lse, d_lse[:, [4, 7]], atol=1e-13)
+
+
+def test_mask_empty_context_printed_test(golden):
+    """PR #49294 digest, test_mask_empty_context: random LSE/outputs with the
+    empty request's rows NaN; afterwards those rows are (-inf, 0) and every
+    other value is unchanged."""
+    g = golden("empty_context_rows.json")
+    H, T, D = g["num_heads"], g["num_tokens"], g["head_dim"]
+    qsl = np.concatenate([[0], np.cumsum(g["query_lens"])])
+    csl = np.concatenate([[0], np.cumsum(g["context_lens"])])
+    rng = np.random.default_rng(0)
+    lse = rng.standard_normal((H, T)).astype(np.float32)
+    out = rng.standard_normal((T, H, D)).astype(np.float32)
+    e0, e1 = g["empty_rows"]
+    out[e0:e1] = np.nan
+    exp_lse, exp_out = lse.copy(), out.copy()
+    exp_lse[:, e0:e1] = -np.inf
+    exp_out[e0:e1] = 0.0
+    O.mask_empty_context(lse, out, qsl, csl)
+    assert np.array_equal(lse, exp_lse) and np.array_equal(out, exp_out)
+
+
+def test_mask_then_merge_equals_init_partial():
+    """Both mechanisms give the same context partial: chunk results merged
+    into an uninitialised partial after masking the empty rows equal the
+    init-then-accumulate path."""
+    wl = W.named_workloads()[2]
+    b = W.make_batch(wl)
+    r = O.chunked_prefill(*_arrays(b), wl.workspace_rows, wl.split_alignment, wl.scale)
+    md = r["metadata"]
+    # partial built the P1 way: start from garbage, every chunk writes its rows,
+    # then rows of requests without context are masked
+    out = np.full_like(r["partial_out"], np.nan)
+    lse = np.full_like(r["partial_lse"], np.nan)
+    for ch in md.chunks:
+        t0, t1 = ch.token_slice
+        out[t0:t1] = r["partial_out"][t0:t1]
+        lse[:, t0:t1] = r["partial_lse"][:, t0:t1]
+    csl = np.concatenate([[0], np.cumsum(wl.context_lens)])
+    O.mask_empty_context(lse, out, md.query_start_loc, csl)
+    assert np.array_equal(out, r["partial_out"]) and np.array_equal(lse, r["partial_lse"])

@@ -21,6 +21,7 @@ Every floating-point step is float64.  Modules:
   merge      LSE merge, partial init/accumulate, thresholded final merge
   pipeline   the chunked prefill end to end, and the direct definition
   mask       mask_empty_context (the earlier mechanism for empty rows)
+  uniform_window  the earlier equal-window scheduler, with the mask in its loop
 """
 from .planner import (ChunkPlan, ContextChunk, ChunkedContextMetadata, aligned_split_len,
                       plan_mla_context_chunks, build_mla_chunked_context_metadata,
@@ -30,11 +31,13 @@ from .merge import (merge_states, merge_attn_states, init_mla_context_partial,
                     accumulate_mla_context_chunk)
 from .pipeline import chunked_prefill, direct_prefill, direct_rows
 from .mask import mask_empty_context
+from .uniform_window import plan_uniform_windows, uniform_window_prefill, uniform_window_size
 
 __all__ = [
     "ChunkPlan", "ContextChunk", "ChunkedContextMetadata", "aligned_split_len",
     "plan_mla_context_chunks", "build_mla_chunked_context_metadata", "build_chunked_context",
     "gather_context_rows", "attention_with_lse", "merge_states", "merge_attn_states",
     "init_mla_context_partial", "accumulate_mla_context_chunk", "chunked_prefill",
-    "direct_prefill", "direct_rows", "mask_empty_context",
+    "direct_prefill", "direct_rows", "mask_empty_context", "plan_uniform_windows",
+    "uniform_window_prefill", "uniform_window_size",
 ]

@@ -9,9 +9,14 @@ synthetic and already resident in HBM when the timed region starts.
 Prints one JSON line.  `value` is the whole step's attention throughput:
 algorithmic flops of chunk + suffix attention per second (2*(192+128) flops
 per unmasked (query, key, head)).  `roofline` is for the dominant kernel
-(chunk attention), timed live with HIP events on its own stream over the
-timed region.  `cpu_baseline` times the fp64 oracle on a bounded sample of
-the same workload on the host cores.
+(the kernel kind with the most time), timed live with HIP events on its own
+stream over the timed region.  `cpu_baseline` times the fp64 oracle on a
+bounded sample of the same workload on the host cores.
+
+--path uniform_window times the earlier equal-window scheduler
+(mla_uniform_window_prefill) instead and also times the chunked path on the
+same batch, reporting both latencies.  --path mask_empty_context times the
+empty-context mask alone (one launch over the batch per step).
 """
 import argparse
 import json
@@ -34,7 +39,7 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def work_figures(wl, chunks):
+def work_figures(wl, chunks, windows=None):
     H = wl.num_heads
     ctx = wl.context_lens
     ql = wl.query_lens
@@ -47,12 +52,25 @@ def work_figures(wl, chunks):
     final_merge_bytes = T * H * merge_row
     cont_rows = sum(ql[c["request_begin"]] for c in chunks if c["is_continuation"])
     accumulate_bytes = cont_rows * H * merge_row
+    mask_bytes = 0
+    if windows is not None:  # uniform-window scheduler: whole-batch merges and masks
+        accumulate_bytes = max(0, len(windows) - 1) * T * H * merge_row
+        qsl = [0]
+        for x in ql:
+            qsl.append(qsl[-1] + x)
+        for lens in windows:
+            if any(x == 0 for x in lens):
+                rows = sum(ql[r] for r in range(len(ql)) if lens[r] == 0)
+                mask_bytes += rows * H * (128 * 2 + 4) + (len(ql) + 1) * 8
     # chunk attention must read Q, the gathered K/V rows and write O + LSE
-    q_rows = sum(sum(ql[c["request_begin"]:c["request_end"]]) for c in chunks)
+    if windows is None:
+        q_rows = sum(sum(ql[c["request_begin"]:c["request_end"]]) for c in chunks)
+    else:
+        q_rows = len(windows) * T
     chunk_bytes = H * (q_rows * (192 * 2 + 128 * 2 + 4) + rows * (192 + 128) * 2)
     return dict(chunk_flops=chunk_flops, suffix_flops=suffix_flops, gather_bytes=gather_bytes, chunk_bytes=chunk_bytes,
                 merge_bytes=final_merge_bytes + accumulate_bytes, final_merge_bytes=final_merge_bytes,
-                accumulate_bytes=accumulate_bytes)
+                accumulate_bytes=accumulate_bytes, mask_bytes=mask_bytes)
 
 
 def profiled_traffic(kernel, workload):
@@ -77,7 +95,7 @@ def profiled_traffic(kernel, workload):
     return k["fetch_bytes_per_launch"] + k["write_bytes_per_launch"]
 
 
-def cpu_baseline(b, wl, sample_queries):
+def cpu_baseline(b, wl, sample_queries, path="chunked"):
     """The oracle on a bounded sample: head 0 only and the first
     `sample_queries` new tokens of every request, against full contexts."""
     import numpy as np
@@ -100,36 +118,141 @@ def cpu_baseline(b, wl, sample_queries):
     kc = f(b.k_cache[:, :, 0:1].contiguous())
     vc = f(b.v_cache[:, :, 0:1].contiguous())
     bt = b.block_table.cpu().numpy()
+    run = oracle.chunked_prefill if path == "chunked" else oracle.uniform_window_prefill
     t0 = time.perf_counter()
-    oracle.chunked_prefill(q, kn, vn, kc, vc, bt, wl.block_size, wl.context_lens, sq, wl.workspace_rows,
-                           wl.split_alignment, wl.scale)
+    run(q, kn, vn, kc, vc, bt, wl.block_size, wl.context_lens, sq, wl.workspace_rows, wl.split_alignment, wl.scale)
     dt = time.perf_counter() - t0
     flops = FLOP_PER_PAIR * (sum(a * c for a, c in zip(sq, wl.context_lens)) + sum(a * (a + 1) // 2 for a in sq))
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
             "seconds": round(dt, 3),
             "sample": f"head 0 of {wl.num_heads}, first {sample_queries} new tokens of each of the "
-                      f"{wl.num_requests} requests against their full contexts (fp64 NumPy, whole chunked "
-                      f"path: plan, gather, chunk attention, merges, causal suffix); value = sample flops / time"}
+                      f"{wl.num_requests} requests against their full contexts (fp64 NumPy, whole {path} "
+                      f"path: plan, gather, context attention, merges, causal suffix); value = sample flops / "
+                      f"time"}
 
 
-def main():
+def mask_cpu_baseline(wl, heads=8):
+    """The oracle's mask over all tokens of `heads` heads (fp64), repeated
+    for about two seconds; value scaled to all heads as GB/s of the rows it
+    writes."""
+    import numpy as np
+    import oracle
+    ql, ctx = wl.query_lens, wl.context_lens
+    qsl = np.concatenate([[0], np.cumsum(ql)])
+    csl = np.concatenate([[0], np.cumsum(ctx)])
+    T = wl.num_tokens
+    lse = np.zeros((heads, T))
+    out = np.zeros((T, heads, 128))
+    n, t0 = 0, time.perf_counter()
+    while True:
+        oracle.mask_empty_context(lse, out, qsl, csl)
+        n += 1
+        if time.perf_counter() - t0 > 2.0:
+            break
+    dt = (time.perf_counter() - t0) / n
+    rows = sum(q for q, c in zip(ql, ctx) if c == 0)
+    gbs = rows * wl.num_heads * (128 * 2 + 4) / (dt * wl.num_heads / heads) / 1e9
+    return {"value": round(gbs, 3), "unit": "GB/s", "cores": 1, "kind": "oracle", "seconds": round(dt * n, 3),
+            "sample": f"{heads} of {wl.num_heads} heads, all {T} tokens, {n} repetitions (fp64 NumPy); time "
+                      f"scaled by heads; bytes counted as the bf16 rows + fp32 LSE the kernel writes"}
+
+
+def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--workload", default="long_context",
-                    choices=["tiny", "empty_context_stress", "homogeneous", "heterogeneous", "long_context"])
+    ap.add_argument("--workload", default=None,
+                    choices=["tiny", "empty_context_stress", "homogeneous", "heterogeneous", "long_context"],
+                    help="default: long_context (chunked), heterogeneous (uniform_window, mask_empty_context)")
+    ap.add_argument("--path", default="chunked", choices=["chunked", "uniform_window", "mask_empty_context"])
     ap.add_argument("--cpu-sample-queries", type=int, default=8192)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibration-copy-mb", type=int, default=0,
                     help="after timing, run one elementwise copy (negation) of this many MiB of bf16 so that "
                          "hardware byte counters can be scaled against a kernel of known traffic")
     args = ap.parse_args()
+    if args.workload is None:
+        args.workload = "long_context" if args.path == "chunked" else "heterogeneous"
+    return args
+
+
+def timed_steps(mla, torch, step, steps, warmup):
+    """W untimed steps, then K steps bracketed by device syncs, with every
+    library kernel timed by HIP events on its own stream."""
+    log(f"bench: warmup {warmup}")
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"bench: timing {steps} steps")
+    mla.mla_kernel_timing_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    kt = mla.mla_kernel_timing_read()
+    mla.mla_kernel_timing_enable(False)
+    return (t1 - t0) / steps * 1e3, kt
+
+
+KIND_WORK = {  # kernel kind -> (work figure, unit, bound)
+    "chunk_attn": ("chunk_flops", "TFLOP/s", "mfma"), "suffix_attn": ("suffix_flops", "TFLOP/s", "mfma"),
+    "gather": ("gather_bytes", "GB/s", "hbm"), "merge": ("merge_bytes", "GB/s", "hbm"),
+    "mask": ("mask_bytes", "GB/s", "hbm"), "init": (None, None, "hbm"),
+}
+KIND_KERNEL = {"chunk_attn": "chunk_attention_kernel", "suffix_attn": "suffix_attention_kernel",
+               "gather": "gather_kernel", "merge": "merge_kernel_d128", "mask": "mask_empty_context_kernel",
+               "init": "init_partial_kernel"}
+
+
+def kernel_table(kt, wf, K):
+    kernels = {}
+    for kind, (work, unit, _) in KIND_WORK.items():
+        n, tms = kt[kind]
+        if n == 0:
+            continue
+        e = {"launches_per_step": n / K, "ms_per_step": round(tms / K, 4)}
+        if work is not None and tms > 0 and wf.get(work):
+            rate = wf[work] * K / (tms / 1e3) / (1e12 if unit == "TFLOP/s" else 1e9)
+            peak = PEAK_BF16_TFLOPS if unit == "TFLOP/s" else PEAK_HBM_GBS
+            e.update({"achieved": round(rate, 2), "unit": unit, "frac_of_peak": round(rate / peak, 4)})
+        kernels[kind] = e
+    return kernels
+
+
+def roofline(kt, wf, K, workload, kind=None):
+    """Roofline entry of the kernel kind with the most time (or `kind`)."""
+    if kind is None:
+        kind = max((k for k in KIND_WORK if KIND_WORK[k][0] is not None), key=lambda k: kt[k][1])
+    work, unit, bound = KIND_WORK[kind]
+    n, tms = kt[kind]
+    per_launch = wf[work] * K / n if n else None
+    achieved = wf[work] * K / (tms / 1e3) / (1e12 if unit == "TFLOP/s" else 1e9) if tms > 0 else None
+    peak = PEAK_BF16_TFLOPS if unit == "TFLOP/s" else PEAK_HBM_GBS
+    r = {"kernel": kind, "bound": bound, "achieved": round(achieved, 2) if achieved else None, "peak": peak,
+         "unit": unit, "frac": round(achieved / peak, 4) if achieved else None,
+         "traffic": profiled_traffic(KIND_KERNEL[kind], workload),
+         "traffic_unit": "bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
+         "launches_per_step": n / K, "avg_launch_ms": round(tms / n, 4) if n else None}
+    if unit == "TFLOP/s":
+        r["flops_per_launch"] = per_launch
+        if kind == "chunk_attn":
+            r["algorithmic_bytes_per_launch"] = wf["chunk_bytes"] * K / n if n else None
+    else:
+        r["algorithmic_bytes_per_launch"] = per_launch
+    return r
+
+
+def main():
+    args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print(f"bench.py runs on one GPU only: the chunked-prefill path here is single-GPU "
               f"(asked for --gpus {args.gpus}); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
+    import numpy as np
     import torch
     import workloads as W
     import mla_chunked_context_amd as mla
@@ -140,74 +263,75 @@ def main():
     log(f"bench: generating {wl.name} inputs on the GPU")
     b = W.make_batch(wl, device=dev, canary=False)
     T, H = wl.num_tokens, wl.num_heads
+    K = args.steps
     out = torch.empty((T, H, W.DV), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((H, T), dtype=torch.float32, device=dev)
-    p = mla.make_prefill_params(b.q, b.k_new, b.v_new, b.k_cache, b.v_cache, b.block_table, wl.context_lens,
-                                wl.query_lens, wl.workspace_rows, wl.split_alignment, wl.scale, out=out, out_lse=lse)
-    scratch = torch.empty(mla.mla_chunked_prefill_scratch_size(p), dtype=torch.uint8, device=dev)
-    p = mla.make_prefill_params(b.q, b.k_new, b.v_new, b.k_cache, b.v_cache, b.block_table, wl.context_lens,
-                                wl.query_lens, wl.workspace_rows, wl.split_alignment, wl.scale, out=out, out_lse=lse,
-                                scratch=scratch)
     chunks, _, _ = mla.mla_plan_context_chunks(wl.context_lens, wl.query_lens, wl.workspace_rows, 0,
                                                wl.split_alignment)
-    wf = work_figures(wl, chunks)
-    stream = torch.cuda.current_stream()
+    config = {"workload": wl.name, "num_requests": wl.num_requests, "query_lens": list(wl.query_lens),
+              "context_lens": list(wl.context_lens), "num_heads": H, "qk_head_dim": 192, "v_head_dim": 128,
+              "workspace_rows": wl.workspace_rows, "split_alignment": wl.split_alignment,
+              "block_size": wl.block_size, "tokens": T, "context_rows": sum(wl.context_lens),
+              "chunks": len(chunks), "continuation_chunks": sum(c["is_continuation"] for c in chunks),
+              "value_std": wl.std, "path": args.path}
 
-    log(f"bench: warmup {args.warmup}")
-    for _ in range(args.warmup):
-        mla.mla_chunked_prefill(p)
-    torch.cuda.synchronize()
+    def prefill_step(path):
+        size = {"chunked": mla.mla_chunked_prefill_scratch_size,
+                "uniform_window": mla.mla_uniform_window_prefill_scratch_size}[path]
+        run = {"chunked": mla.mla_chunked_prefill, "uniform_window": mla.mla_uniform_window_prefill}[path]
+        mk = lambda s=None: mla.make_prefill_params(  # noqa: E731
+            b.q, b.k_new, b.v_new, b.k_cache, b.v_cache, b.block_table, wl.context_lens, wl.query_lens,
+            wl.workspace_rows, wl.split_alignment, wl.scale, out=out, out_lse=lse, scratch=s)
+        scratch = torch.empty(size(mk()), dtype=torch.uint8, device=dev)
+        p = mk(scratch)
+        return (lambda: run(p)), scratch
 
-    log(f"bench: timing {args.steps} steps")
-    mla.mla_kernel_timing_enable(True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        mla.mla_chunked_prefill(p)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    kt = mla.mla_kernel_timing_read()
-    mla.mla_kernel_timing_enable(False)
-    assert torch.isfinite(lse).all().item(), "non-finite LSE in the benchmark output"
-
-    K = args.steps
-    ms = (t1 - t0) / K * 1e3
-    value = (wf["chunk_flops"] + wf["suffix_flops"]) / (ms / 1e3) / 1e12
-    n_ca, ms_ca = kt["chunk_attn"]
-    ca_tflops = wf["chunk_flops"] * K / (ms_ca / 1e3) / 1e12 if ms_ca > 0 else None
-    kernels = {}
-    for kind, work, unit in (("chunk_attn", wf["chunk_flops"], "TFLOP/s"),
-                             ("suffix_attn", wf["suffix_flops"], "TFLOP/s"),
-                             ("gather", wf["gather_bytes"], "GB/s"), ("merge", wf["merge_bytes"], "GB/s"),
-                             ("init", None, None)):
-        n, tms = kt[kind]
-        e = {"launches_per_step": n / K, "ms_per_step": round(tms / K, 4)}
-        if work is not None and tms > 0:
-            rate = work * K / (tms / 1e3) / (1e12 if unit == "TFLOP/s" else 1e9)
-            peak = PEAK_BF16_TFLOPS if unit == "TFLOP/s" else PEAK_HBM_GBS
-            e.update({"achieved": round(rate, 2), "unit": unit, "frac_of_peak": round(rate / peak, 4)})
-        kernels[kind] = e
+    extra = {}
+    if args.path == "mask_empty_context":
+        qsl = torch.tensor(np.concatenate([[0], np.cumsum(wl.query_lens)]), dtype=torch.int32, device=dev)
+        csl = torch.tensor(np.concatenate([[0], np.cumsum(wl.context_lens)]), dtype=torch.int32, device=dev)
+        lse.zero_()
+        out.zero_()
+        ms, kt = timed_steps(mla, torch, lambda: mla.mla_mask_empty_context(lse, out, qsl, csl), K, args.warmup)
+        rows = sum(q for q, c in zip(wl.query_lens, wl.context_lens) if c == 0)
+        wf = {"mask_bytes": rows * H * (128 * 2 + 4) + (wl.num_requests + 1) * 8}
+        n, tms = kt["mask"]
+        value = wf["mask_bytes"] * K / (tms / 1e3) / 1e9
+        metric, unit = "mask_empty_context GB/s (rows written)", "GB/s"
+        rf = roofline(kt, wf, K, wl.name, kind="mask")
+        rf["masked_rows"] = rows
+        kernels = kernel_table(kt, wf, K)
+        steps_desc = "one mask launch over the batch"
+    else:
+        windows = None
+        if args.path == "uniform_window":
+            w, iters = mla.mla_plan_uniform_windows(wl.context_lens, wl.workspace_rows, wl.split_alignment)
+            # rows of each request's window per iteration, for the work figures
+            windows = [[max(0, min(c, (i + 1) * w) - i * w) for c in wl.context_lens] for i in range(iters)]
+            config.update({"window": w, "iterations": iters})
+        wf = work_figures(wl, chunks, windows)
+        step, scratch = prefill_step(args.path)
+        ms, kt = timed_steps(mla, torch, step, K, args.warmup)
+        assert torch.isfinite(lse).all().item(), "non-finite LSE in the benchmark output"
+        value = (wf["chunk_flops"] + wf["suffix_flops"]) / (ms / 1e3) / 1e12
+        metric, unit = METRIC, "TFLOP/s"
+        rf = roofline(kt, wf, K, wl.name)
+        kernels = kernel_table(kt, wf, K)
+        steps_desc = "the whole path over one batch"
+        del scratch
+        if args.path == "uniform_window":
+            step_c, scratch_c = prefill_step("chunked")
+            ms_c, _ = timed_steps(mla, torch, step_c, K, args.warmup)
+            del scratch_c
+            extra["compare"] = {"uniform_window_ms_per_step": round(ms, 3), "chunked_ms_per_step": round(ms_c, 3),
+                                "chunked_speedup": round(ms / ms_c, 3), "iterations": config["iterations"],
+                                "chunks": len(chunks)}
 
     res = {
-        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": K,
+        "metric": metric, "value": round(value, 2), "unit": unit, "n_gpus": 1, "steps": K,
         "warmup": args.warmup, "ms_per_step": round(ms, 3), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": wl.name, "num_requests": wl.num_requests, "query_lens": list(wl.query_lens),
-                   "context_lens": list(wl.context_lens), "num_heads": H, "qk_head_dim": 192, "v_head_dim": 128,
-                   "workspace_rows": wl.workspace_rows, "split_alignment": wl.split_alignment,
-                   "block_size": wl.block_size, "tokens": T, "context_rows": sum(wl.context_lens),
-                   "chunks": len(chunks), "continuation_chunks": sum(c["is_continuation"] for c in chunks),
-                   "value_std": wl.std},
-        "roofline": {"kernel": "chunk_attn", "bound": "mfma",
-                     "achieved": round(ca_tflops, 2) if ca_tflops else None, "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(ca_tflops / PEAK_BF16_TFLOPS, 4) if ca_tflops else None,
-                     "traffic": profiled_traffic("chunk_attention_kernel", wl.name),
-                     "traffic_unit": "bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
-                     "algorithmic_bytes_per_launch": (wf["chunk_bytes"] / n_ca * K) if n_ca else None,
-                     "launches_per_step": n_ca / K,
-                     "flops_per_launch": wf["chunk_flops"] * K / n_ca if n_ca else None,
-                     "avg_launch_ms": round(ms_ca / n_ca, 4) if n_ca else None},
-        "kernels": kernels,
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic", "step": steps_desc,
+        "config": config, "roofline": rf, "kernels": kernels, **extra,
     }
     if args.calibration_copy_mb > 0:
         n = args.calibration_copy_mb * (1 << 20) // 2
@@ -218,11 +342,13 @@ def main():
         torch.cuda.synchronize()
         res["calibration_copy_bytes"] = {"read": n * 2, "write": n * 2}
         del src, dst
-    del scratch
     torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         log("bench: cpu baseline (oracle sample)")
-        res["cpu_baseline"] = cpu_baseline(b, wl, args.cpu_sample_queries)
+        if args.path == "mask_empty_context":
+            res["cpu_baseline"] = mask_cpu_baseline(wl)
+        else:
+            res["cpu_baseline"] = cpu_baseline(b, wl, args.cpu_sample_queries, args.path)
     print(json.dumps(res), flush=True)
 
 

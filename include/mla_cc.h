@@ -270,6 +270,37 @@ int mla_chunked_prefill_scratch_size(const mla_chunked_prefill_params* params, i
 int mla_chunked_prefill(const mla_chunked_prefill_params* params, void* stream);
 
 /*
+ * The uniform-window context scheduler that per-request packing replaced
+ * (PR #50613 digest, 功能与动机): the workspace_rows are shared equally by
+ * the requests with context, each getting a window of
+ *   window = floor(floor(workspace_rows / n_ctx) / split_alignment) * split_alignment
+ * rows, and iteration i covers context rows [i*window, (i+1)*window) of every
+ * request; there are ceil(max context / window) iterations.  Host only, pure.
+ * window = num_iterations = 0 when no request has context.
+ * MLA_ERR_INVALID_ARG when the share holds no aligned window (the earlier
+ * scheduler needed at least one aligned window per request with context).
+ */
+int mla_plan_uniform_windows(const int32_t* context_lens, int32_t num_requests, int64_t workspace_rows,
+                             int32_t split_alignment, int64_t* window, int32_t* num_iterations);
+
+/* Scratch bytes mla_uniform_window_prefill needs (host only). */
+int mla_uniform_window_prefill_scratch_size(const mla_chunked_prefill_params* params, int64_t* bytes);
+
+/*
+ * The whole context prefill under the uniform-window scheduler, with the
+ * PR #49294 digest's loop (实现拆解 item 2): per iteration, gather every
+ * request's window, attention of the whole prefill batch against its windows,
+ * mla_mask_empty_context over the iteration's result when any window is
+ * empty, and (from the second iteration on) merge_attn_states of the running
+ * context state with it over all tokens.  Then the causal suffix attention
+ * and the final merge with prefix_num_tokens, as in mla_chunked_prefill.
+ * Same params and conventions as mla_chunked_prefill (max_context_chunk is
+ * not used; split_alignment rounds the window).  Kept to measure the
+ * scheduler change; it computes the same result up to rounding.
+ */
+int mla_uniform_window_prefill(const mla_chunked_prefill_params* params, void* stream);
+
+/*
  * Kernel timing, a measurement aid (not part of the method).  While enabled,
  * every kernel the library launches is bracketed by a pair of HIP events
  * recorded on the launch's own stream.  mla_kernel_timing_read waits for the

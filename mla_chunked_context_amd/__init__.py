@@ -82,6 +82,9 @@ _merge = _sig("mla_merge_attn_states", _ptr, _ptr, _ptr, _ptr, _ptr, _ptr, _i64,
 _mask = _sig("mla_mask_empty_context", _ptr, _i64, _ptr, _i32, _ptr, _ptr, _i32, _i64, _i32, _i32, _ptr)
 _scratch_size = _sig("mla_chunked_prefill_scratch_size", ctypes.POINTER(ChunkedPrefillParams), _i64p)
 _prefill = _sig("mla_chunked_prefill", ctypes.POINTER(ChunkedPrefillParams), _ptr)
+_plan_windows = _sig("mla_plan_uniform_windows", _i32p, _i32, _i64, _i32, _i64p, _i32p)
+_uw_scratch_size = _sig("mla_uniform_window_prefill_scratch_size", ctypes.POINTER(ChunkedPrefillParams), _i64p)
+_uw_prefill = _sig("mla_uniform_window_prefill", ctypes.POINTER(ChunkedPrefillParams), _ptr)
 
 class KernelTime(ctypes.Structure):
     _fields_ = [("launches", ctypes.c_int64), ("total_ms", ctypes.c_double)]
@@ -95,7 +98,8 @@ EXPORTED = [
     "mla_status_string", "mla_abi_version", "mla_plan_context_chunks", "mla_prefill_token_info",
     "mla_init_context_partial", "mla_gather_context", "mla_context_chunk_attn", "mla_causal_suffix_attn",
     "mla_merge_attn_states", "mla_chunked_prefill_scratch_size", "mla_chunked_prefill",
-    "mla_kernel_timing_enable", "mla_kernel_timing_read", "mla_mask_empty_context",
+    "mla_kernel_timing_enable", "mla_kernel_timing_read", "mla_mask_empty_context", "mla_plan_uniform_windows",
+    "mla_uniform_window_prefill_scratch_size", "mla_uniform_window_prefill",
 ]
 
 
@@ -160,6 +164,15 @@ def mla_prefill_token_info(context_lens, query_lens):
     _check(_token_info(ctx_p, ql_p, len(ctx), ctypes.byref(pnt), sl.ctypes.data_as(_i32p), ne.value,
                        ctypes.byref(ne)), "mla_prefill_token_info")
     return pnt.value, [(int(sl[2 * i]), int(sl[2 * i + 1])) for i in range(ne.value)]
+
+
+def mla_plan_uniform_windows(context_lens, workspace_rows, split_alignment=64):
+    """Returns (window, num_iterations) of the uniform-window scheduler."""
+    ctx, ctx_p = _i32_array(context_lens)
+    w, it = _i64(0), _i32(0)
+    _check(_plan_windows(ctx_p, len(ctx), workspace_rows, split_alignment, ctypes.byref(w), ctypes.byref(it)),
+           "mla_plan_uniform_windows")
+    return w.value, it.value
 
 
 # ---------------------------------------------------------------- device
@@ -263,6 +276,16 @@ def mla_chunked_prefill_scratch_size(params: ChunkedPrefillParams) -> int:
 
 def mla_chunked_prefill(params: ChunkedPrefillParams, stream=None):
     _check(_prefill(ctypes.byref(params), _stream(stream)), "mla_chunked_prefill")
+
+
+def mla_uniform_window_prefill_scratch_size(params: ChunkedPrefillParams) -> int:
+    n = _i64(0)
+    _check(_uw_scratch_size(ctypes.byref(params), ctypes.byref(n)), "mla_uniform_window_prefill_scratch_size")
+    return n.value
+
+
+def mla_uniform_window_prefill(params: ChunkedPrefillParams, stream=None):
+    _check(_uw_prefill(ctypes.byref(params), _stream(stream)), "mla_uniform_window_prefill")
 
 
 def mla_kernel_timing_enable(enable: bool = True):

@@ -108,17 +108,24 @@ __device__ __forceinline__ float pair_sum(float x) {
     return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
 }
 
-// Workgroups are dealt to the 8 XCDs round-robin; map them so that each XCD
-// processes a contiguous range of logical tiles.
-__device__ __forceinline__ int32_t xcd_logical_tile(int32_t bid, int32_t total) {
-    const int32_t per = total / kNumXcd;
-    if (bid >= per * kNumXcd) return bid;
-    return (bid % kNumXcd) * per + bid / kNumXcd;
+// Workgroups are dealt to the 8 XCDs round-robin (XCD = bid % 8, and each
+// XCD starts its share in bid order).  Logical tiles are (group, q tile) with
+// group = (sequence, head).  XCD x takes groups x, x + 8, x + 16, ... with all
+// q tiles of a group back to back, so the tiles that stream the same K/V rows
+// run together under one L2, and every sequence's heads are spread evenly
+// over the XCDs whatever the sequence lengths.  Groups past the last full set
+// of 8 keep the identity mapping.
+__device__ __forceinline__ int32_t xcd_logical_tile(int32_t bid, int32_t total, int32_t q_tiles) {
+    const int32_t groups = total / q_tiles;
+    const int32_t full = groups / kNumXcd * kNumXcd;
+    if (bid >= full * q_tiles) return bid;
+    const int32_t x = bid % kNumXcd, j = bid / kNumXcd;
+    return (x + kNumXcd * (j / q_tiles)) * q_tiles + j % q_tiles;
 }
 
 template <bool kCausal>
 __device__ __forceinline__ void attention_body(const AttnArgs& a, unsigned char* k_lds, bf16_t* vt_lds) {
-    const int32_t tile = xcd_logical_tile(blockIdx.x, a.total_tiles);
+    const int32_t tile = xcd_logical_tile(blockIdx.x, a.total_tiles, a.q_tiles);
     int32_t qt = tile % a.q_tiles;
     const int32_t rest = tile / a.q_tiles;
     const int32_t head = rest % a.heads;

@@ -202,6 +202,101 @@ int check_params(const mla_chunked_prefill_params* p) {
         if (st_ != MLA_OK) return st_;    \
     } while (0)
 
+// ---------------------------------------------------------------------------
+// Uniform-window scheduler (the scheduling per-request packing replaced,
+// PR #50613 digest, 功能与动机): every iteration covers the same window of
+// every request and runs attention, mask and merge over the whole batch.
+
+struct WindowProblem {
+    int64_t window = 0;
+    int32_t iterations = 0;
+    std::vector<int32_t> meta;  // e_req[N], qsl[N+1], per iteration e_start[N] and e_off[N+1]
+    int64_t e_req = 0, qsl = 0;
+    std::vector<int64_t> it_start, it_off;
+    std::vector<int32_t> it_rows;
+    std::vector<char> it_has_empty;
+    int64_t tokens = 0;
+    int32_t max_q = 0;
+    int64_t prefix_num_tokens = 0;
+    Layout lay{};
+};
+
+int build_window_problem(const mla_chunked_prefill_params& p, WindowProblem& pb) {
+    const int32_t n = p.num_requests;
+    MLA_TRY(uniform_windows(p.context_lens, n, p.workspace_rows, p.split_alignment, &pb.window, &pb.iterations));
+    int32_t n_empty = 0;
+    const int st = token_info(p.context_lens, p.query_lens, n, &pb.prefix_num_tokens, nullptr, 0, &n_empty);
+    if (st != MLA_OK && st != MLA_ERR_CAPACITY) return st;
+
+    pb.e_req = static_cast<int64_t>(pb.meta.size());
+    for (int32_t r = 0; r < n; ++r) pb.meta.push_back(r);
+    pb.qsl = static_cast<int64_t>(pb.meta.size());
+    int64_t tok = 0;
+    pb.meta.push_back(0);
+    for (int32_t r = 0; r < n; ++r) {
+        tok += p.query_lens[r];
+        pb.meta.push_back(static_cast<int32_t>(tok));
+        pb.max_q = std::max(pb.max_q, p.query_lens[r]);
+    }
+    pb.tokens = tok;
+
+    int64_t max_rows = 0;
+    const int64_t w = pb.window;
+    for (int32_t it = 0; it < pb.iterations; ++it) {
+        pb.it_start.push_back(static_cast<int64_t>(pb.meta.size()));
+        for (int32_t r = 0; r < n; ++r) pb.meta.push_back(static_cast<int32_t>(it * w));
+        pb.it_off.push_back(static_cast<int64_t>(pb.meta.size()));
+        int64_t off = 0;
+        bool empty = false;
+        pb.meta.push_back(0);
+        for (int32_t r = 0; r < n; ++r) {
+            const int64_t len = std::max<int64_t>(0, std::min<int64_t>(p.context_lens[r], (it + 1) * w) - it * w);
+            empty = empty || len == 0;
+            off += len;
+            pb.meta.push_back(static_cast<int32_t>(off));
+        }
+        pb.it_rows.push_back(static_cast<int32_t>(off));
+        pb.it_has_empty.push_back(empty ? 1 : 0);
+        max_rows = std::max(max_rows, off);
+    }
+
+    const int64_t H = p.num_heads, T = pb.tokens;
+    Layout& L = pb.lay;
+    int64_t o = 0;
+    auto take = [&](int64_t bytes) {
+        const int64_t at = o;
+        o = round_up(o + std::max<int64_t>(bytes, 0), kAlign);
+        return at;
+    };
+    L.ws_k = take(max_rows * H * kDk * 2);
+    L.ws_v = take(max_rows * H * kDv * 2);
+    L.part_out = take(T * H * kDv * 2);
+    L.part_lse = take(H * T * 4);
+    L.suf_out = take(T * H * kDv * 2);
+    L.suf_lse = take(H * T * 4);
+    L.tmp_rows = pb.iterations > 1 ? T : 0;
+    L.tmp_out = take(L.tmp_rows * H * kDv * 2);
+    L.tmp_lse = take(H * L.tmp_rows * 4);
+    L.meta_ints = static_cast<int64_t>(pb.meta.size());
+    L.meta = take(L.meta_ints * 4);
+    L.total = o;
+    return MLA_OK;
+}
+
+// Pointer checks shared by both drivers.
+int check_buffers(const mla_chunked_prefill_params& p, bool needs_cache, int64_t scratch_needed) {
+    if (p.q == nullptr || p.k_new == nullptr || p.v_new == nullptr || p.out == nullptr || p.scratch == nullptr)
+        return MLA_ERR_INVALID_ARG;
+    if (!aligned16(p.q) || !aligned16(p.k_new) || !aligned16(p.v_new) || !aligned16(p.out) ||
+        (reinterpret_cast<uintptr_t>(p.scratch) % kAlign) != 0)
+        return MLA_ERR_INVALID_ARG;
+    if (needs_cache && (p.k_cache == nullptr || p.v_cache == nullptr || p.block_table == nullptr ||
+                        !aligned16(p.k_cache) || !aligned16(p.v_cache)))
+        return MLA_ERR_INVALID_ARG;
+    if (p.scratch_bytes < scratch_needed) return MLA_ERR_CAPACITY;
+    return MLA_OK;
+}
+
 }  // namespace
 
 }  // namespace mla
@@ -226,17 +321,7 @@ int mla_chunked_prefill(const mla_chunked_prefill_params* params, void* stream_v
     const int64_t T = pb.tokens;
     const int32_t H = p.num_heads;
     if (T == 0) return MLA_OK;
-    if (p.q == nullptr || p.k_new == nullptr || p.v_new == nullptr || p.out == nullptr || p.scratch == nullptr)
-        return MLA_ERR_INVALID_ARG;
-    if (!aligned16(p.q) || !aligned16(p.k_new) || !aligned16(p.v_new) || !aligned16(p.out) ||
-        (reinterpret_cast<uintptr_t>(p.scratch) % kAlign) != 0)
-        return MLA_ERR_INVALID_ARG;
-    if (!pb.plan.chunks.empty()) {
-        if (p.k_cache == nullptr || p.v_cache == nullptr || p.block_table == nullptr || !aligned16(p.k_cache) ||
-            !aligned16(p.v_cache))
-            return MLA_ERR_INVALID_ARG;
-    }
-    if (p.scratch_bytes < pb.lay.total) return MLA_ERR_CAPACITY;
+    MLA_TRY(check_buffers(p, !pb.plan.chunks.empty(), pb.lay.total));
 
     hipStream_t stream = static_cast<hipStream_t>(stream_v);
     char* base = static_cast<char*>(p.scratch);
@@ -293,6 +378,68 @@ int mla_chunked_prefill(const mla_chunked_prefill_params* params, void* stream_v
     const int32_t* scu = meta + pb.suffix_cu;
     MLA_TRY(launch_attention(q, static_cast<const bf16_t*>(p.k_new), static_cast<const bf16_t*>(p.v_new), scu, scu,
                              p.num_requests, pb.max_q, H, p.scale, true, suf_out, suf_lse, T, stream));
+    MLA_TRY(launch_merge(static_cast<bf16_t*>(p.out), p.out_lse, part_out, part_lse, suf_out, suf_lse, T, H, kDv,
+                         T, T, T, pb.prefix_num_tokens, stream));
+    return MLA_OK;
+}
+
+}  // extern "C"
+
+extern "C" {
+
+int mla_uniform_window_prefill_scratch_size(const mla_chunked_prefill_params* params, int64_t* bytes) {
+    if (bytes == nullptr) return MLA_ERR_INVALID_ARG;
+    MLA_TRY(mla::check_params(params));
+    mla::WindowProblem pb;
+    MLA_TRY(mla::build_window_problem(*params, pb));
+    *bytes = pb.lay.total;
+    return MLA_OK;
+}
+
+int mla_uniform_window_prefill(const mla_chunked_prefill_params* params, void* stream_v) {
+    using namespace mla;
+    MLA_TRY(check_params(params));
+    const mla_chunked_prefill_params& p = *params;
+    WindowProblem pb;
+    MLA_TRY(build_window_problem(p, pb));
+    const int64_t T = pb.tokens;
+    const int32_t H = p.num_heads, N = p.num_requests;
+    if (T == 0) return MLA_OK;
+    MLA_TRY(check_buffers(p, pb.iterations > 0, pb.lay.total));
+
+    hipStream_t stream = static_cast<hipStream_t>(stream_v);
+    char* base = static_cast<char*>(p.scratch);
+    const Layout& L = pb.lay;
+    bf16_t* ws_k = reinterpret_cast<bf16_t*>(base + L.ws_k);
+    bf16_t* ws_v = reinterpret_cast<bf16_t*>(base + L.ws_v);
+    bf16_t* part_out = reinterpret_cast<bf16_t*>(base + L.part_out);
+    float* part_lse = reinterpret_cast<float*>(base + L.part_lse);
+    bf16_t* suf_out = reinterpret_cast<bf16_t*>(base + L.suf_out);
+    float* suf_lse = reinterpret_cast<float*>(base + L.suf_lse);
+    bf16_t* tmp_out = reinterpret_cast<bf16_t*>(base + L.tmp_out);
+    float* tmp_lse = reinterpret_cast<float*>(base + L.tmp_lse);
+    int32_t* meta = reinterpret_cast<int32_t*>(base + L.meta);
+
+    MLA_TRY(upload(pb.meta.data(), pb.meta.size() * sizeof(int32_t), meta, stream));
+    const bf16_t* q = static_cast<const bf16_t*>(p.q);
+    const int32_t* qsl = meta + pb.qsl;
+
+    for (int32_t it = 0; it < pb.iterations; ++it) {
+        const int32_t* e_off = meta + pb.it_off[it];
+        MLA_TRY(launch_gather(static_cast<const bf16_t*>(p.k_cache), static_cast<const bf16_t*>(p.v_cache),
+                              p.num_blocks, p.block_size, H, p.block_table, p.block_table_width, meta + pb.e_req,
+                              meta + pb.it_start[it], e_off, N, pb.it_rows[it], ws_k, ws_v, stream));
+        // iteration 0 is the context state itself; later ones go through the temporary
+        bf16_t* o = it == 0 ? part_out : tmp_out;
+        float* l = it == 0 ? part_lse : tmp_lse;
+        MLA_TRY(launch_attention(q, ws_k, ws_v, qsl, e_off, N, pb.max_q, H, p.scale, false, o, l, T, stream));
+        if (pb.it_has_empty[it]) MLA_TRY(launch_mask_empty_context(l, T, o, 2, qsl, e_off, N, T, H, kDv, stream));
+        if (it > 0) MLA_TRY(launch_merge(part_out, part_lse, part_out, part_lse, tmp_out, tmp_lse, T, H, kDv, T, T, T,
+                                         T, stream));
+    }
+
+    MLA_TRY(launch_attention(q, static_cast<const bf16_t*>(p.k_new), static_cast<const bf16_t*>(p.v_new), qsl, qsl,
+                             N, pb.max_q, H, p.scale, true, suf_out, suf_lse, T, stream));
     MLA_TRY(launch_merge(static_cast<bf16_t*>(p.out), p.out_lse, part_out, part_lse, suf_out, suf_lse, T, H, kDv,
                          T, T, T, pb.prefix_num_tokens, stream));
     return MLA_OK;

@@ -136,6 +136,26 @@ int token_info(const int32_t* ctx, const int32_t* qlens, int32_t n, int64_t* pre
     return count > cap ? MLA_ERR_CAPACITY : MLA_OK;
 }
 
+int uniform_windows(const int32_t* ctx, int32_t n, int64_t budget, int32_t align, int64_t* window,
+                    int32_t* iterations) {
+    if (n < 0 || budget < 1 || align < 1 || window == nullptr || iterations == nullptr) return MLA_ERR_INVALID_ARG;
+    if (n > 0 && ctx == nullptr) return MLA_ERR_INVALID_ARG;
+    int64_t with_ctx = 0, longest = 0;
+    for (int32_t r = 0; r < n; ++r) {
+        if (ctx[r] < 0) return MLA_ERR_INVALID_ARG;
+        if (ctx[r] > 0) ++with_ctx;
+        longest = std::max<int64_t>(longest, ctx[r]);
+    }
+    *window = 0;
+    *iterations = 0;
+    if (with_ctx == 0) return MLA_OK;
+    const int64_t w = budget / with_ctx / align * align;
+    if (w < 1) return MLA_ERR_INVALID_ARG;
+    *window = w;
+    *iterations = static_cast<int32_t>((longest + w - 1) / w);
+    return MLA_OK;
+}
+
 }  // namespace mla
 
 // ----------------------------------------------------------------------------
@@ -213,6 +233,12 @@ int mla_prefill_token_info(const int32_t* context_lens, const int32_t* query_len
                            int32_t* num_empty) {
     return mla::token_info(context_lens, query_lens, num_requests, prefix_num_tokens, empty_slices,
                            empty_capacity, num_empty);
+}
+
+int mla_plan_uniform_windows(const int32_t* context_lens, int32_t num_requests, int64_t workspace_rows,
+                             int32_t split_alignment, int64_t* window, int32_t* num_iterations) {
+    return mla::uniform_windows(context_lens, num_requests, workspace_rows, split_alignment, window,
+                                num_iterations);
 }
 
 }  // extern "C"

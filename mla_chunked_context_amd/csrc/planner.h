@@ -25,4 +25,11 @@ int plan_chunks(const int32_t* ctx, const int32_t* qlens, int32_t n, int64_t bud
 int token_info(const int32_t* ctx, const int32_t* qlens, int32_t n, int64_t* prefix_num_tokens,
                int32_t* empty, int32_t cap, int32_t* num_empty);
 
+// Window of the uniform-window scheduler: the workspace shared equally by the
+// requests with context, rounded down to the alignment.  window = 0 and
+// iterations = 0 when no request has context; MLA_ERR_INVALID_ARG when the
+// share holds no aligned window.
+int uniform_windows(const int32_t* ctx, int32_t n, int64_t budget, int32_t align, int64_t* window,
+                    int32_t* iterations);
+
 }  // namespace mla

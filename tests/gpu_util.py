@@ -11,6 +11,7 @@ import sys
 import numpy as np
 import torch
 
+import oracle as O
 import workloads as W
 
 OUT_TOL = 2e-2
@@ -22,20 +23,24 @@ def say(*a):
     sys.stdout.flush()
 
 
-def run_prefill(mla, b, out_lse=True, stream=None):
-    """Run mla_chunked_prefill on a Batch that lives on the GPU."""
+def run_prefill(mla, b, out_lse=True, stream=None, path="chunked"):
+    """Run the whole path (mla_chunked_prefill, or mla_uniform_window_prefill
+    with path="uniform_window") on a Batch that lives on the GPU."""
+    size = {"chunked": mla.mla_chunked_prefill_scratch_size,
+            "uniform_window": mla.mla_uniform_window_prefill_scratch_size}[path]
+    run = {"chunked": mla.mla_chunked_prefill, "uniform_window": mla.mla_uniform_window_prefill}[path]
     wl = b.wl
     T, H = wl.num_tokens, wl.num_heads
     out = torch.full((T, H, W.DV), float("nan"), dtype=torch.bfloat16, device=b.q.device)
     lse = torch.full((H, T), float("nan"), dtype=torch.float32, device=b.q.device) if out_lse else None
     p = mla.make_prefill_params(b.q, b.k_new, b.v_new, b.k_cache, b.v_cache, b.block_table, wl.context_lens,
                                 wl.query_lens, wl.workspace_rows, wl.split_alignment, wl.scale, out=out, out_lse=lse)
-    nbytes = mla.mla_chunked_prefill_scratch_size(p)
+    nbytes = size(p)
     scratch = torch.full(((max(nbytes, 256) + 1) // 2,), float("nan"), dtype=torch.bfloat16, device=b.q.device)
     p = mla.make_prefill_params(b.q, b.k_new, b.v_new, b.k_cache, b.v_cache, b.block_table, wl.context_lens,
                                 wl.query_lens, wl.workspace_rows, wl.split_alignment, wl.scale, out=out, out_lse=lse,
                                 scratch=scratch)
-    mla.mla_chunked_prefill(p, stream=stream)
+    run(p, stream=stream)
     torch.cuda.synchronize()
     return out, lse
 
@@ -63,3 +68,60 @@ def check(out, lse, ref_out, ref_lse, vmax, what=""):
         assert lerr <= LSE_TOL, f"{what}: LSE error {lerr}"
     assert err <= OUT_TOL, f"{what}: output error {err} x max|V|"
     return res
+
+
+def oracle_inputs(b):
+    f = W.to_f64
+    return (f(b.q), f(b.k_new), f(b.v_new), f(b.k_cache), f(b.v_cache), b.block_table.numpy(),
+            b.wl.block_size, b.wl.context_lens, b.wl.query_lens)
+
+
+def context_rows(b, r, heads):
+    """Context rows 0..c-1 of request r, selected heads, read from the paged
+    cache on the device (host float64 arrays)."""
+    wl = b.wl
+    c = wl.context_lens[r]
+    nb = (c + wl.block_size - 1) // wl.block_size
+    blocks = b.block_table[r, :nb].long()
+    hs = torch.tensor(heads, device=b.k_cache.device)
+    k = b.k_cache.index_select(0, blocks).index_select(2, hs).reshape(nb * wl.block_size, len(heads), W.DK)[:c]
+    v = b.v_cache.index_select(0, blocks).index_select(2, hs).reshape(nb * wl.block_size, len(heads), W.DV)[:c]
+    return host(k), host(v)
+
+
+def sampled_check(mla, wl, tokens_per_request=6, seed=0, path="chunked", device="cuda:0"):
+    """Full-size run of a workload, checked on sampled rows (first, last,
+    middle and random tokens of each request; a few heads) against the direct
+    definition computed one row at a time, plus no-NaN / finite-LSE everywhere."""
+    say(f"{path} full size {wl.name}: N={wl.num_requests} T={wl.num_tokens} ctx={sum(wl.context_lens)}")
+    b = W.make_batch(wl, device=device, canary=False)
+    out, lse = run_prefill(mla, b, path=path)
+    say("  ran; checking")
+    assert not torch.isnan(out).any().item() and torch.isfinite(lse).all().item()
+    rng = np.random.default_rng(seed)
+    H = wl.num_heads
+    heads = sorted({0, H - 1, int(rng.integers(0, H)), int(rng.integers(0, H))})
+    qsl = np.concatenate([[0], np.cumsum(wl.query_lens)])
+    worst = {"out_err_over_vmax": 0.0, "lse_err": 0.0}
+    hs = torch.tensor(heads, device=device)
+    for r in range(wl.num_requests):
+        n = wl.query_lens[r]
+        if n == 0:
+            continue
+        pos = sorted({0, n - 1, n // 2, *[int(x) for x in rng.integers(0, n, size=max(0, tokens_per_request - 3))]})
+        kc, vc = context_rows(b, r, heads)
+        a = int(qsl[r])
+        kn = host(b.k_new[a:a + max(pos) + 1].index_select(1, hs))
+        vn = host(b.v_new[a:a + max(pos) + 1].index_select(1, hs))
+        qr = host(b.q[[a + p for p in pos]].index_select(1, hs))
+        ref_o, ref_l = O.direct_rows(qr, pos, kc, vc, kn, vn, wl.scale)
+        got_o = host(out[[a + p for p in pos]].index_select(1, hs))
+        got_l = lse.index_select(0, hs)[:, [a + p for p in pos]].double().cpu().numpy()
+        vmax = float(max(np.abs(vc).max(initial=0), np.abs(vn).max()))
+        res = check(got_o, got_l, ref_o, ref_l, vmax, f"{wl.name} request {r}")
+        for k in worst:
+            worst[k] = max(worst[k], res[k])
+    say("  worst", worst)
+    del b, out, lse
+    torch.cuda.empty_cache()
+    return worst

@@ -189,3 +189,47 @@ def test_mask_rejects_bad_arguments_without_gpu():
                                     None) == 1  # element size 3
     assert f.mla_mask_empty_context(None, ctypes.c_int64(8), ctypes.c_void_p(256), 4, ctypes.c_void_p(256),
                                     ctypes.c_void_p(256), 2, ctypes.c_int64(8), 2, 16, None) == 1
+
+
+def test_uniform_windows_match_oracle():
+    rng = np.random.default_rng(11)
+    for _ in range(3000):
+        n = int(rng.integers(0, 40))
+        ctx = [0 if rng.random() < 0.3 else int(rng.integers(1, 5000)) for _ in range(n)]
+        a = int(rng.choice([1, 16, 64]))
+        n_ctx = sum(c > 0 for c in ctx)
+        rows = int(rng.integers(1, max(2, n_ctx) * a * 50))
+        try:
+            w_ref, _, lens = O.plan_uniform_windows(ctx, rows, a)
+        except ValueError:
+            with pytest.raises(mla.MlaError):
+                mla.mla_plan_uniform_windows(ctx, rows, a)
+            continue
+        assert mla.mla_plan_uniform_windows(ctx, rows, a) == (w_ref, len(lens)), (ctx, rows, a)
+    for wl in W.named_workloads().values():
+        if wl.name == "empty_context_stress":
+            continue  # 33 requests with context share 256 rows: no 16-row window
+        w_ref, _, lens = O.plan_uniform_windows(wl.context_lens, wl.workspace_rows, wl.split_alignment)
+        assert mla.mla_plan_uniform_windows(wl.context_lens, wl.workspace_rows, wl.split_alignment) == \
+            (w_ref, len(lens))
+
+
+def test_uniform_window_prefill_host_checks():
+    wl = W.named_workloads()[4]
+    p = mla.ChunkedPrefillParams()
+    ctx = np.asarray(wl.context_lens, dtype=np.int32)
+    ql = np.asarray(wl.query_lens, dtype=np.int32)
+    p.context_lens, p.query_lens, p.num_requests = ctx.ctypes.data, ql.ctypes.data, len(ctx)
+    p.num_heads, p.block_size, p.block_table_width, p.num_blocks = 128, 64, 4096, 8192
+    p.scale, p.workspace_rows, p.split_alignment = wl.scale, wl.workspace_rows, 64
+    n = mla.mla_uniform_window_prefill_scratch_size(p)
+    T, H = wl.num_tokens, 128
+    w, _ = mla.mla_plan_uniform_windows(wl.context_lens, wl.workspace_rows, 64)
+    n_ctx = sum(c > 0 for c in wl.context_lens)
+    assert n >= 4 * T * H * 260 and n <= 4 * T * H * 260 + n_ctx * w * H * 640 + 64 * 4096
+    p.scratch_bytes = n
+    with pytest.raises(mla.MlaError):  # null device pointers
+        mla.mla_uniform_window_prefill(p, stream=0)
+    p.workspace_rows = n_ctx * 64 - 1  # below one aligned window per request
+    with pytest.raises(mla.MlaError):
+        mla.mla_uniform_window_prefill_scratch_size(p)

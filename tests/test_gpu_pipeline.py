@@ -9,15 +9,13 @@ oracle.
   few heads) against the direct definition computed one row at a time, plus
   properties that hold at any size (no NaN, finite LSE everywhere).
 """
-import math
-
 import numpy as np
 import pytest
 import torch
 
 import oracle as O
 import workloads as W
-from tests.gpu_util import check, host, run_prefill, say
+from tests.gpu_util import check, host, oracle_inputs, run_prefill, sampled_check, say
 
 pytestmark = pytest.mark.gpu
 
@@ -29,15 +27,9 @@ import mla_chunked_context_amd as mla  # noqa: E402
 DEV = "cuda:0"
 
 
-def _oracle_inputs(b):
-    f = W.to_f64
-    return (f(b.q), f(b.k_new), f(b.v_new), f(b.k_cache), f(b.v_cache), b.block_table.numpy(),
-            b.wl.block_size, b.wl.context_lens, b.wl.query_lens)
-
-
 def _full_case(wl):
     b = W.make_batch(wl, device="cpu", canary=True)
-    ref = O.chunked_prefill(*_oracle_inputs(b), wl.workspace_rows, wl.split_alignment, wl.scale)
+    ref = O.chunked_prefill(*oracle_inputs(b), wl.workspace_rows, wl.split_alignment, wl.scale)
     d = W.Batch(wl, b.q.to(DEV), b.k_new.to(DEV), b.v_new.to(DEV), b.k_cache.to(DEV), b.v_cache.to(DEV),
                 b.block_table.to(DEV), b.num_blocks, b.spare_blocks)
     out, lse = run_prefill(mla, d)
@@ -79,60 +71,13 @@ def test_run_twice_is_bitwise_identical():
 # ------------------------------------------------------------- full sizes
 
 
-def _context_rows(b, r, heads):
-    wl = b.wl
-    c = wl.context_lens[r]
-    nb = (c + wl.block_size - 1) // wl.block_size
-    blocks = b.block_table[r, :nb].long()
-    hs = torch.tensor(heads, device=b.k_cache.device)
-    k = b.k_cache.index_select(0, blocks).index_select(2, hs).reshape(nb * wl.block_size, len(heads), W.DK)[:c]
-    v = b.v_cache.index_select(0, blocks).index_select(2, hs).reshape(nb * wl.block_size, len(heads), W.DV)[:c]
-    return host(k), host(v)
-
-
-def _sampled_check(idx, requests=None, tokens_per_request=6, seed=0):
-    wl = W.named_workloads()[idx]
-    say(f"pipeline full size {wl.name}: N={wl.num_requests} T={wl.num_tokens} ctx={sum(wl.context_lens)}")
-    b = W.make_batch(wl, device=DEV, canary=False)
-    out, lse = run_prefill(mla, b)
-    say("  ran; checking")
-    assert not torch.isnan(out).any().item() and torch.isfinite(lse).all().item()
-    rng = np.random.default_rng(seed)
-    H = wl.num_heads
-    heads = sorted({0, H - 1, int(rng.integers(0, H)), int(rng.integers(0, H))})
-    qsl = np.concatenate([[0], np.cumsum(wl.query_lens)])
-    reqs = range(wl.num_requests) if requests is None else requests
-    worst = {"out_err_over_vmax": 0.0, "lse_err": 0.0}
-    hs = torch.tensor(heads, device=DEV)
-    for r in reqs:
-        n = wl.query_lens[r]
-        if n == 0:
-            continue
-        pos = sorted({0, n - 1, n // 2, *[int(x) for x in rng.integers(0, n, size=max(0, tokens_per_request - 3))]})
-        kc, vc = _context_rows(b, r, heads)
-        a = int(qsl[r])
-        kn = host(b.k_new[a:a + max(pos) + 1].index_select(1, hs))
-        vn = host(b.v_new[a:a + max(pos) + 1].index_select(1, hs))
-        qr = host(b.q[[a + p for p in pos]].index_select(1, hs))
-        ref_o, ref_l = O.direct_rows(qr, pos, kc, vc, kn, vn, wl.scale)
-        got_o = host(out[[a + p for p in pos]].index_select(1, hs))
-        got_l = lse.index_select(0, hs)[:, [a + p for p in pos]].double().cpu().numpy()
-        vmax = float(max(np.abs(vc).max(initial=0), np.abs(vn).max()))
-        res = check(got_o, got_l, ref_o, ref_l, vmax, f"{wl.name} request {r}")
-        for k in worst:
-            worst[k] = max(worst[k], res[k])
-    say("  worst", worst)
-    del b, out, lse
-    torch.cuda.empty_cache()
-
-
 def test_homogeneous_full_size_sampled():
-    _sampled_check(3)
+    sampled_check(mla, W.named_workloads()[3])
 
 
 def test_heterogeneous_full_size_sampled():
-    _sampled_check(4, tokens_per_request=4)
+    sampled_check(mla, W.named_workloads()[4], tokens_per_request=4)
 
 
 def test_long_context_full_size_sampled():
-    _sampled_check(5, tokens_per_request=8)
+    sampled_check(mla, W.named_workloads()[5], tokens_per_request=8)

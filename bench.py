@@ -16,7 +16,10 @@ bounded sample of the same workload on the host cores.
 --path uniform_window times the earlier equal-window scheduler
 (mla_uniform_window_prefill) instead and also times the chunked path on the
 same batch, reporting both latencies.  --path mask_empty_context times the
-empty-context mask alone (one launch over the batch per step).
+empty-context mask alone (one launch over the batch per step).  --path dcp
+times mla_dcp_chunked_prefill with the context sharded over --dcp-world
+emulated ranks (every rank's local gather runs on this one GPU), beside the
+single-device path on the same batch.
 """
 import argparse
 import json
@@ -95,7 +98,7 @@ def profiled_traffic(kernel, workload):
     return k["fetch_bytes_per_launch"] + k["write_bytes_per_launch"]
 
 
-def cpu_baseline(b, wl, sample_queries, path="chunked"):
+def cpu_baseline(b, wl, sample_queries, path="chunked", rank_caches=None, dcp=(1, 1)):
     """The oracle on a bounded sample: head 0 only and the first
     `sample_queries` new tokens of every request, against full contexts."""
     import numpy as np
@@ -118,10 +121,21 @@ def cpu_baseline(b, wl, sample_queries, path="chunked"):
     kc = f(b.k_cache[:, :, 0:1].contiguous())
     vc = f(b.v_cache[:, :, 0:1].contiguous())
     bt = b.block_table.cpu().numpy()
-    run = oracle.chunked_prefill if path == "chunked" else oracle.uniform_window_prefill
-    t0 = time.perf_counter()
-    run(q, kn, vn, kc, vc, bt, wl.block_size, wl.context_lens, sq, wl.workspace_rows, wl.split_alignment, wl.scale)
-    dt = time.perf_counter() - t0
+    if path == "dcp":
+        import oracle.dcp
+        lk = [f(r.k_cache[:, :, 0:1].contiguous()) for r in rank_caches]
+        lv = [f(r.v_cache[:, :, 0:1].contiguous()) for r in rank_caches]
+        lt = [r.block_table.cpu().numpy() for r in rank_caches]
+        t0 = time.perf_counter()
+        oracle.dcp.dcp_chunked_prefill(q, kn, vn, lk, lv, lt, wl.block_size, wl.context_lens, sq, wl.workspace_rows,
+                                       wl.split_alignment, wl.scale, dcp[0], dcp[1])
+        dt = time.perf_counter() - t0
+    else:
+        run = oracle.chunked_prefill if path == "chunked" else oracle.uniform_window_prefill
+        t0 = time.perf_counter()
+        run(q, kn, vn, kc, vc, bt, wl.block_size, wl.context_lens, sq, wl.workspace_rows, wl.split_alignment,
+            wl.scale)
+        dt = time.perf_counter() - t0
     flops = FLOP_PER_PAIR * (sum(a * c for a, c in zip(sq, wl.context_lens)) + sum(a * (a + 1) // 2 for a in sq))
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
             "seconds": round(dt, 3),
@@ -165,7 +179,9 @@ def parse():
     ap.add_argument("--workload", default=None,
                     choices=["tiny", "empty_context_stress", "homogeneous", "heterogeneous", "long_context"],
                     help="default: long_context (chunked), heterogeneous (uniform_window, mask_empty_context)")
-    ap.add_argument("--path", default="chunked", choices=["chunked", "uniform_window", "mask_empty_context"])
+    ap.add_argument("--path", default="chunked", choices=["chunked", "uniform_window", "mask_empty_context", "dcp"])
+    ap.add_argument("--dcp-world", type=int, default=4, help="emulated DCP ranks (--path dcp)")
+    ap.add_argument("--dcp-interleave", type=int, default=1, help="DCP interleave run length (--path dcp)")
     ap.add_argument("--cpu-sample-queries", type=int, default=8192)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibration-copy-mb", type=int, default=0,
@@ -200,11 +216,12 @@ def timed_steps(mla, torch, step, steps, warmup):
 KIND_WORK = {  # kernel kind -> (work figure, unit, bound)
     "chunk_attn": ("chunk_flops", "TFLOP/s", "mfma"), "suffix_attn": ("suffix_flops", "TFLOP/s", "mfma"),
     "gather": ("gather_bytes", "GB/s", "hbm"), "merge": ("merge_bytes", "GB/s", "hbm"),
-    "mask": ("mask_bytes", "GB/s", "hbm"), "init": (None, None, "hbm"),
+    "mask": ("mask_bytes", "GB/s", "hbm"), "dcp_reorg": ("reorg_bytes", "GB/s", "hbm"),
+    "init": (None, None, "hbm"),
 }
 KIND_KERNEL = {"chunk_attn": "chunk_attention_kernel", "suffix_attn": "suffix_attention_kernel",
                "gather": "gather_kernel", "merge": "merge_kernel_d128", "mask": "mask_empty_context_kernel",
-               "init": "init_partial_kernel"}
+               "dcp_reorg": "dcp_reorganize_kernel", "init": "init_partial_kernel"}
 
 
 def kernel_table(kt, wf, K):
@@ -275,13 +292,18 @@ def main():
               "chunks": len(chunks), "continuation_chunks": sum(c["is_continuation"] for c in chunks),
               "value_std": wl.std, "path": args.path}
 
-    def prefill_step(path):
-        size = {"chunked": mla.mla_chunked_prefill_scratch_size,
-                "uniform_window": mla.mla_uniform_window_prefill_scratch_size}[path]
-        run = {"chunked": mla.mla_chunked_prefill, "uniform_window": mla.mla_uniform_window_prefill}[path]
+    def prefill_step(path, ranks=None):
         mk = lambda s=None: mla.make_prefill_params(  # noqa: E731
             b.q, b.k_new, b.v_new, b.k_cache, b.v_cache, b.block_table, wl.context_lens, wl.query_lens,
             wl.workspace_rows, wl.split_alignment, wl.scale, out=out, out_lse=lse, scratch=s)
+        if path == "dcp":
+            scratch = torch.empty(mla.mla_dcp_chunked_prefill_scratch_size(mk(), ranks), dtype=torch.uint8,
+                                  device=dev)
+            p = mk(scratch)
+            return (lambda: mla.mla_dcp_chunked_prefill(p, ranks)), scratch
+        size = {"chunked": mla.mla_chunked_prefill_scratch_size,
+                "uniform_window": mla.mla_uniform_window_prefill_scratch_size}[path]
+        run = {"chunked": mla.mla_chunked_prefill, "uniform_window": mla.mla_uniform_window_prefill}[path]
         scratch = torch.empty(size(mk()), dtype=torch.uint8, device=dev)
         p = mk(scratch)
         return (lambda: run(p)), scratch
@@ -310,7 +332,19 @@ def main():
             windows = [[max(0, min(c, (i + 1) * w) - i * w) for c in wl.context_lens] for i in range(iters)]
             config.update({"window": w, "iterations": iters})
         wf = work_figures(wl, chunks, windows)
-        step, scratch = prefill_step(args.path)
+        dranks = rank_caches = None
+        if args.path == "dcp":
+            D, il = args.dcp_world, args.dcp_interleave
+            log(f"bench: sharding the context over {D} emulated ranks")
+            rank_caches = W.shard_context(b, D, il, canary=False)
+            dranks = mla.make_dcp_ranks(rank_caches, il)
+            dch, *_ = mla.mla_plan_dcp_context_chunks(wl.context_lens, wl.query_lens, wl.workspace_rows, D, il, 0,
+                                                      wl.split_alignment)
+            # local gathers move every rank's padded rows; the reorganisation moves the context rows
+            wf["gather_bytes"] = 2 * H * 640 * sum(c["num_rows"] for c in dch)
+            wf["reorg_bytes"] = 2 * H * 640 * sum(wl.context_lens)
+            config.update({"dcp_world": D, "dcp_interleave": il, "dcp_chunks": len(dch)})
+        step, scratch = prefill_step(args.path, dranks)
         ms, kt = timed_steps(mla, torch, step, K, args.warmup)
         assert torch.isfinite(lse).all().item(), "non-finite LSE in the benchmark output"
         value = (wf["chunk_flops"] + wf["suffix_flops"]) / (ms / 1e3) / 1e12
@@ -319,13 +353,17 @@ def main():
         kernels = kernel_table(kt, wf, K)
         steps_desc = "the whole path over one batch"
         del scratch
-        if args.path == "uniform_window":
+        if args.path in ("uniform_window", "dcp"):
             step_c, scratch_c = prefill_step("chunked")
             ms_c, _ = timed_steps(mla, torch, step_c, K, args.warmup)
             del scratch_c
-            extra["compare"] = {"uniform_window_ms_per_step": round(ms, 3), "chunked_ms_per_step": round(ms_c, 3),
-                                "chunked_speedup": round(ms / ms_c, 3), "iterations": config["iterations"],
-                                "chunks": len(chunks)}
+            if args.path == "uniform_window":
+                extra["compare"] = {"uniform_window_ms_per_step": round(ms, 3), "chunked_ms_per_step": round(ms_c, 3),
+                                    "chunked_speedup": round(ms / ms_c, 3), "iterations": config["iterations"],
+                                    "chunks": len(chunks)}
+            else:
+                extra["compare"] = {"dcp_ms_per_step": round(ms, 3), "single_device_ms_per_step": round(ms_c, 3),
+                                    "dcp_chunks": config["dcp_chunks"], "chunks": len(chunks)}
 
     res = {
         "metric": metric, "value": round(value, 2), "unit": unit, "n_gpus": 1, "steps": K,
@@ -348,7 +386,9 @@ def main():
         if args.path == "mask_empty_context":
             res["cpu_baseline"] = mask_cpu_baseline(wl)
         else:
-            res["cpu_baseline"] = cpu_baseline(b, wl, args.cpu_sample_queries, args.path)
+            res["cpu_baseline"] = cpu_baseline(b, wl, args.cpu_sample_queries, args.path,
+                                               rank_caches if args.path == "dcp" else None,
+                                               (args.dcp_world, args.dcp_interleave))
     print(json.dumps(res), flush=True)
 
 

@@ -106,6 +106,32 @@ int mla_plan_context_chunks(const int32_t* context_lens, const int32_t* query_le
                             int32_t* num_entries);
 
 /*
+ * Chunk planning with the context sharded over DCP ranks (PR #50613 digest:
+ * the planner's padded_rows hook in 关键源码片段; local chunks with
+ * padded_local_* and local_starts in 风险与影响; DCP local chunk data in the
+ * test file of 实现拆解 item 5).  The pages print neither the sharding nor
+ * padded_rows; this library reads them as follows.  Position p of a request's
+ * context lives on rank (p / interleave) % world_size at local index
+ * (p / (interleave * world_size)) * interleave + p % interleave.  Every rank
+ * reserves padded_local(x) = interleave * ceil(x / (interleave * world_size))
+ * local rows for positions [0, x), and chunks are packed by rows of the
+ * all-gathered workspace, padded_rows(x) = world_size * padded_local(x).
+ * Otherwise as mla_plan_context_chunks; split_alignment must be a multiple of
+ * world_size * interleave (else MLA_ERR_INVALID_ARG).  Per entry it also
+ * returns local_start = start / world_size and the padded local length
+ * padded_local(start + seq_len) - local_start (the same on every rank);
+ * mla_chunk_desc.num_rows is the chunk's all-gathered rows, world_size times
+ * the sum of its local lengths.  world_size = interleave = 1 gives exactly
+ * mla_plan_context_chunks.
+ */
+int mla_plan_dcp_context_chunks(const int32_t* context_lens, const int32_t* query_lens, int32_t num_requests,
+                                int64_t row_budget, int64_t max_context_chunk, int32_t split_alignment,
+                                int32_t world_size, int32_t interleave, mla_chunk_desc* chunks,
+                                int32_t chunk_capacity, int32_t* num_chunks, int32_t* entry_starts,
+                                int32_t* entry_seq_lens, int32_t* entry_local_starts, int32_t* entry_local_lens,
+                                int32_t entry_capacity, int32_t* num_entries);
+
+/*
  * Batch-wide token fields (PR #36540 digest, 实现拆解; PR #50613 digest,
  * 实现拆解 item 1).  Host only.
  *   *prefix_num_tokens  prefill_tokens_with_context: query_start_loc just past
@@ -153,6 +179,25 @@ int mla_gather_context(const void* k_cache, const void* v_cache, int64_t num_blo
                        const int32_t* entry_request, const int32_t* entry_starts,
                        const int32_t* entry_row_offsets, int32_t num_entries, int32_t num_rows,
                        void* ws_k, void* ws_v, void* stream);
+
+/*
+ * Reorganise an all-gathered DCP workspace into request order (the step after
+ * the all-gather on the PR #50613 digest's DCP path, 风险与影响; layout as in
+ * mla_plan_dcp_context_chunks).  gathered_k/v stack world_size rank
+ * workspaces of local_rows rows; in rank r's block, entry e's padded local
+ * rows start at entry_local_offsets[e].  Output row w of entry e
+ * (entry_row_offsets[e] <= w < entry_row_offsets[e+1]) is context position
+ * entry_starts[e] + w - entry_row_offsets[e], copied from its rank's block.
+ *   gathered_k  dev bf16 [world_size * local_rows, H, 192]   gathered_v  [.., H, 128]
+ *   entry_starts, entry_row_offsets (num_entries + 1), entry_local_offsets  dev int32
+ *   ws_k / ws_v dev bf16 [num_rows, H, 192] / [num_rows, H, 128]
+ * A row whose source falls outside the gathered buffer is written as NaN.
+ */
+int mla_dcp_reorganize_context(const void* gathered_k, const void* gathered_v, int32_t num_heads,
+                               int32_t world_size, int32_t interleave, int32_t local_rows,
+                               const int32_t* entry_starts, const int32_t* entry_row_offsets,
+                               const int32_t* entry_local_offsets, int32_t num_entries, int32_t num_rows,
+                               void* ws_k, void* ws_v, void* stream);
 
 /*
  * Varlen non-causal attention of one chunk (run_prefill_context_chunk on the
@@ -301,6 +346,38 @@ int mla_uniform_window_prefill_scratch_size(const mla_chunked_prefill_params* pa
 int mla_uniform_window_prefill(const mla_chunked_prefill_params* params, void* stream);
 
 /*
+ * DCP ranks emulated on one device: the context cache of each rank (its
+ * positions of every request, in order, in its own paged cache and block
+ * table).  Host arrays of world_size entries.
+ */
+typedef struct mla_dcp_ranks {
+    int32_t world_size;
+    int32_t interleave;
+    const void* const* k_cache;        /* [r]: dev bf16 [num_blocks[r], block_size, H, 192] */
+    const void* const* v_cache;        /* [r]: dev bf16 [num_blocks[r], block_size, H, 128] */
+    const int32_t* const* block_table; /* [r]: dev int32 [num_requests, block_table_width[r]] */
+    const int64_t* num_blocks;
+    const int32_t* block_table_width;
+} mla_dcp_ranks;
+
+/* Scratch bytes mla_dcp_chunked_prefill needs (host only). */
+int mla_dcp_chunked_prefill_scratch_size(const mla_chunked_prefill_params* params, const mla_dcp_ranks* ranks,
+                                         int64_t* bytes);
+
+/*
+ * mla_chunked_prefill with each chunk's context rows assembled as under DCP
+ * (PR #50613 digest, 风险与影响): chunks from mla_plan_dcp_context_chunks;
+ * per chunk every rank gathers its padded local rows into its block of the
+ * gathered workspace (which is where an all-gather would put them), then
+ * mla_dcp_reorganize_context restores request order, then attention and
+ * accumulate as in mla_chunked_prefill.  The params' k_cache, v_cache,
+ * block_table, num_blocks and block_table_width are not used; block_size
+ * applies to every rank's cache.  The result equals mla_chunked_prefill's on
+ * the unsharded cache up to the rounding of a different chunking.
+ */
+int mla_dcp_chunked_prefill(const mla_chunked_prefill_params* params, const mla_dcp_ranks* ranks, void* stream);
+
+/*
  * Kernel timing, a measurement aid (not part of the method).  While enabled,
  * every kernel the library launches is bracketed by a pair of HIP events
  * recorded on the launch's own stream.  mla_kernel_timing_read waits for the
@@ -316,7 +393,8 @@ enum {
     MLA_KERNEL_SUFFIX_ATTN = 3,
     MLA_KERNEL_MERGE = 4,
     MLA_KERNEL_MASK = 5,
-    MLA_KERNEL_KINDS = 6
+    MLA_KERNEL_DCP_REORG = 6,
+    MLA_KERNEL_KINDS = 7
 };
 
 typedef struct mla_kernel_time {

@@ -53,6 +53,14 @@ class ChunkedPrefillParams(ctypes.Structure):
     ]
 
 
+class DcpRanks(ctypes.Structure):
+    _fields_ = [
+        ("world_size", _i32), ("interleave", _i32), ("k_cache", ctypes.POINTER(_ptr)),
+        ("v_cache", ctypes.POINTER(_ptr)), ("block_table", ctypes.POINTER(_ptr)), ("num_blocks", _i64p),
+        ("block_table_width", _i32p),
+    ]
+
+
 def _sig(name, *argtypes):
     try:
         f = getattr(_lib, name)
@@ -82,6 +90,13 @@ _merge = _sig("mla_merge_attn_states", _ptr, _ptr, _ptr, _ptr, _ptr, _ptr, _i64,
 _mask = _sig("mla_mask_empty_context", _ptr, _i64, _ptr, _i32, _ptr, _ptr, _i32, _i64, _i32, _i32, _ptr)
 _scratch_size = _sig("mla_chunked_prefill_scratch_size", ctypes.POINTER(ChunkedPrefillParams), _i64p)
 _prefill = _sig("mla_chunked_prefill", ctypes.POINTER(ChunkedPrefillParams), _ptr)
+_plan_dcp = _sig("mla_plan_dcp_context_chunks", _i32p, _i32p, _i32, _i64, _i64, _i32, _i32, _i32,
+                 ctypes.POINTER(ChunkDesc), _i32, _i32p, _i32p, _i32p, _i32p, _i32p, _i32, _i32p)
+_dcp_reorg = _sig("mla_dcp_reorganize_context", _ptr, _ptr, _i32, _i32, _i32, _i32, _ptr, _ptr, _ptr, _i32, _i32,
+                  _ptr, _ptr, _ptr)
+_dcp_scratch_size = _sig("mla_dcp_chunked_prefill_scratch_size", ctypes.POINTER(ChunkedPrefillParams),
+                         ctypes.POINTER(DcpRanks), _i64p)
+_dcp_prefill = _sig("mla_dcp_chunked_prefill", ctypes.POINTER(ChunkedPrefillParams), ctypes.POINTER(DcpRanks), _ptr)
 _plan_windows = _sig("mla_plan_uniform_windows", _i32p, _i32, _i64, _i32, _i64p, _i32p)
 _uw_scratch_size = _sig("mla_uniform_window_prefill_scratch_size", ctypes.POINTER(ChunkedPrefillParams), _i64p)
 _uw_prefill = _sig("mla_uniform_window_prefill", ctypes.POINTER(ChunkedPrefillParams), _ptr)
@@ -90,7 +105,7 @@ class KernelTime(ctypes.Structure):
     _fields_ = [("launches", ctypes.c_int64), ("total_ms", ctypes.c_double)]
 
 
-KERNEL_KINDS = ["init", "gather", "chunk_attn", "suffix_attn", "merge", "mask"]
+KERNEL_KINDS = ["init", "gather", "chunk_attn", "suffix_attn", "merge", "mask", "dcp_reorg"]
 _timing_enable = _sig("mla_kernel_timing_enable", ctypes.c_int)
 _timing_read = _sig("mla_kernel_timing_read", ctypes.POINTER(KernelTime))
 
@@ -99,7 +114,8 @@ EXPORTED = [
     "mla_init_context_partial", "mla_gather_context", "mla_context_chunk_attn", "mla_causal_suffix_attn",
     "mla_merge_attn_states", "mla_chunked_prefill_scratch_size", "mla_chunked_prefill",
     "mla_kernel_timing_enable", "mla_kernel_timing_read", "mla_mask_empty_context", "mla_plan_uniform_windows",
-    "mla_uniform_window_prefill_scratch_size", "mla_uniform_window_prefill",
+    "mla_uniform_window_prefill_scratch_size", "mla_uniform_window_prefill", "mla_plan_dcp_context_chunks",
+    "mla_dcp_reorganize_context", "mla_dcp_chunked_prefill_scratch_size", "mla_dcp_chunked_prefill",
 ]
 
 
@@ -164,6 +180,27 @@ def mla_prefill_token_info(context_lens, query_lens):
     _check(_token_info(ctx_p, ql_p, len(ctx), ctypes.byref(pnt), sl.ctypes.data_as(_i32p), ne.value,
                        ctypes.byref(ne)), "mla_prefill_token_info")
     return pnt.value, [(int(sl[2 * i]), int(sl[2 * i + 1])) for i in range(ne.value)]
+
+
+def mla_plan_dcp_context_chunks(context_lens, query_lens, row_budget, world_size, interleave=1,
+                                max_context_chunk=0, split_alignment=64):
+    """Returns (chunks, entry_starts, entry_seq_lens, entry_local_starts, entry_local_lens)."""
+    ctx, ctx_p = _i32_array(context_lens)
+    ql, ql_p = _i32_array(query_lens)
+    n = len(ctx)
+    if len(ql) != n:
+        raise ValueError("context_lens and query_lens differ in length")
+    nc, ne = _i32(0), _i32(0)
+    args = (ctx_p, ql_p, n, row_budget, max_context_chunk, split_alignment, world_size, interleave)
+    st = _plan_dcp(*args, None, 0, ctypes.byref(nc), None, None, None, None, 0, ctypes.byref(ne))
+    if st not in (MLA_OK, MLA_ERR_CAPACITY):
+        _check(st, "mla_plan_dcp_context_chunks")
+    chunks = (ChunkDesc * max(1, nc.value))()
+    arrs = [np.zeros(max(1, ne.value), dtype=np.int32) for _ in range(4)]
+    _check(_plan_dcp(*args, chunks, nc.value, ctypes.byref(nc), *[a.ctypes.data_as(_i32p) for a in arrs], ne.value,
+                     ctypes.byref(ne)), "mla_plan_dcp_context_chunks")
+    out = [{f: getattr(chunks[i], f) for f, _ in ChunkDesc._fields_} for i in range(nc.value)]
+    return (out, *[a[:ne.value].copy() for a in arrs])
 
 
 def mla_plan_uniform_windows(context_lens, workspace_rows, split_alignment=64):
@@ -276,6 +313,43 @@ def mla_chunked_prefill_scratch_size(params: ChunkedPrefillParams) -> int:
 
 def mla_chunked_prefill(params: ChunkedPrefillParams, stream=None):
     _check(_prefill(ctypes.byref(params), _stream(stream)), "mla_chunked_prefill")
+
+
+def mla_dcp_reorganize_context(gathered_k, gathered_v, world_size, interleave, local_rows, entry_starts,
+                               entry_row_offsets, entry_local_offsets, num_rows, ws_k, ws_v, stream=None):
+    """Device tensors; entry arrays int32 on the device."""
+    _check(_dcp_reorg(_dptr(gathered_k), _dptr(gathered_v), gathered_k.shape[1], world_size, interleave, local_rows,
+                      _dptr(entry_starts), _dptr(entry_row_offsets), _dptr(entry_local_offsets),
+                      entry_starts.numel(), num_rows, _dptr(ws_k), _dptr(ws_v), _stream(stream)),
+           "mla_dcp_reorganize_context")
+
+
+def make_dcp_ranks(rank_caches, interleave=1):
+    """DcpRanks over a list of per-rank caches (objects with k_cache, v_cache,
+    block_table tensors).  The returned struct keeps its host arrays alive."""
+    D = len(rank_caches)
+    r = DcpRanks()
+    r.world_size, r.interleave = D, interleave
+    r._k = (_ptr * D)(*[_dptr(x.k_cache) for x in rank_caches])
+    r._v = (_ptr * D)(*[_dptr(x.v_cache) for x in rank_caches])
+    r._t = (_ptr * D)(*[_dptr(x.block_table) for x in rank_caches])
+    r._nb = (_i64 * D)(*[x.k_cache.shape[0] for x in rank_caches])
+    r._w = (_i32 * D)(*[x.block_table.shape[1] for x in rank_caches])
+    r.k_cache, r.v_cache, r.block_table = r._k, r._v, r._t
+    r.num_blocks = ctypes.cast(r._nb, _i64p)
+    r.block_table_width = ctypes.cast(r._w, _i32p)
+    return r
+
+
+def mla_dcp_chunked_prefill_scratch_size(params: ChunkedPrefillParams, ranks: DcpRanks) -> int:
+    n = _i64(0)
+    _check(_dcp_scratch_size(ctypes.byref(params), ctypes.byref(ranks), ctypes.byref(n)),
+           "mla_dcp_chunked_prefill_scratch_size")
+    return n.value
+
+
+def mla_dcp_chunked_prefill(params: ChunkedPrefillParams, ranks: DcpRanks, stream=None):
+    _check(_dcp_prefill(ctypes.byref(params), ctypes.byref(ranks), _stream(stream)), "mla_dcp_chunked_prefill")
 
 
 def mla_uniform_window_prefill_scratch_size(params: ChunkedPrefillParams) -> int:

@@ -51,6 +51,9 @@ int launch_gather(const bf16_t* k_cache, const bf16_t* v_cache, int64_t num_bloc
                   const int32_t* e_start, const int32_t* e_off, int32_t n_entries, int32_t num_rows,
                   bf16_t* ws_k, bf16_t* ws_v, hipStream_t stream);
 
+int launch_dcp_reorganize(const bf16_t* gk, const bf16_t* gv, int32_t heads, int32_t world, int32_t interleave,
+                          int32_t local_rows, const int32_t* e_start, const int32_t* e_off, const int32_t* e_loff,
+                          int32_t n_entries, int32_t num_rows, bf16_t* ws_k, bf16_t* ws_v, hipStream_t stream);
 int launch_mask_empty_context(float* lse, int64_t lse_stride, void* out, int32_t elem_bytes, const int32_t* qsl,
                               const int32_t* csl, int32_t num_requests, int64_t num_tokens, int32_t heads,
                               int32_t head_dim, hipStream_t stream);

@@ -238,6 +238,46 @@ __global__ __launch_bounds__(kThreads) void gather_kernel(
     }
 }
 
+// ---------------------------------------------------------- DCP assembly
+
+// Rows of an all-gathered DCP workspace back in request order.  The gathered
+// buffer stacks `world` rank workspaces of `local_rows` rows each; rank r's
+// block holds, for entry e, its local rows from local start e_start[e]/world
+// at offset e_loff[e].  Output row w of entry e is context position
+// p = e_start[e] + (w - e_off[e]), held by rank (p / il) % world at local index
+// (p / (il * world)) * il + p % il.  Rows are copied like the gather; a source
+// row outside the gathered buffer (inconsistent metadata) is written as NaN.
+__global__ __launch_bounds__(kThreads) void dcp_reorganize_kernel(
+    const uint4* __restrict__ gk, const uint4* __restrict__ gv, int32_t heads, int32_t world, int32_t il,
+    int32_t local_rows, const int32_t* __restrict__ e_start, const int32_t* __restrict__ e_off,
+    const int32_t* __restrict__ e_loff, int32_t n_entries, int32_t num_rows, uint4* __restrict__ ws_k,
+    uint4* __restrict__ ws_v) {
+    const int32_t row0 = blockIdx.x * kGatherRows;
+    if (row0 >= num_rows) return;
+    int32_t lo = 0, hi = n_entries - 1;
+    while (lo < hi) {
+        const int32_t mid = (lo + hi + 1) >> 1;
+        if (e_off[mid] <= row0) lo = mid; else hi = mid - 1;
+    }
+    int32_t e = lo;
+    const int kvec = heads * (kDk / 8), vvec = heads * (kDv / 8);
+    const int64_t total = static_cast<int64_t>(world) * local_rows;
+    for (int rr = 0; rr < kGatherRows; ++rr) {
+        const int32_t w = row0 + rr;
+        if (w >= num_rows) break;
+        while (e + 1 < n_entries && e_off[e + 1] <= w) ++e;
+        const int64_t s = e_start[e];
+        const int64_t p = s + (w - e_off[e]);
+        const int64_t rank = (p / il) % world;
+        const int64_t local = (p / (static_cast<int64_t>(il) * world)) * il + p % il;
+        int64_t src = rank * local_rows + e_loff[e] + (local - s / world);
+        const bool ok = src >= 0 && src < total;
+        if (!ok) src = 0;
+        copy_row(gk + src * kvec, gv + src * vvec, ws_k + static_cast<int64_t>(w) * kvec,
+                 ws_v + static_cast<int64_t>(w) * vvec, kvec, vvec, ok);
+    }
+}
+
 // ---------------------------------------------------------------- mask
 
 // One wave per token row.  The row's request is found by a wavefront-parallel
@@ -321,6 +361,19 @@ int launch_gather(const bf16_t* k_cache, const bf16_t* v_cache, int64_t num_bloc
     hipLaunchKernelGGL(gather_kernel, dim3(grid), dim3(kThreads), 0, stream,
                        reinterpret_cast<const uint4*>(k_cache), reinterpret_cast<const uint4*>(v_cache), num_blocks,
                        block_size, heads, block_table, bt_width, e_req, e_start, e_off, n_entries, num_rows,
+                       reinterpret_cast<uint4*>(ws_k), reinterpret_cast<uint4*>(ws_v));
+    return hip_status(hipGetLastError());
+}
+
+int launch_dcp_reorganize(const bf16_t* gk, const bf16_t* gv, int32_t heads, int32_t world, int32_t interleave,
+                          int32_t local_rows, const int32_t* e_start, const int32_t* e_off, const int32_t* e_loff,
+                          int32_t n_entries, int32_t num_rows, bf16_t* ws_k, bf16_t* ws_v, hipStream_t stream) {
+    if (num_rows <= 0 || n_entries <= 0) return MLA_OK;
+    const unsigned grid = static_cast<unsigned>((num_rows + kGatherRows - 1) / kGatherRows);
+    TimedLaunch timed(MLA_KERNEL_DCP_REORG, stream);
+    hipLaunchKernelGGL(dcp_reorganize_kernel, dim3(grid), dim3(kThreads), 0, stream,
+                       reinterpret_cast<const uint4*>(gk), reinterpret_cast<const uint4*>(gv), heads, world,
+                       interleave, local_rows, e_start, e_off, e_loff, n_entries, num_rows,
                        reinterpret_cast<uint4*>(ws_k), reinterpret_cast<uint4*>(ws_v));
     return hip_status(hipGetLastError());
 }
@@ -412,4 +465,25 @@ extern "C" int mla_mask_empty_context(float* lse, int64_t lse_head_stride, void*
     return mla::launch_mask_empty_context(lse, lse_head_stride, output, elem_bytes, query_start_loc,
                                           context_start_loc, num_requests, num_tokens, num_heads, head_dim,
                                           static_cast<hipStream_t>(stream));
+}
+
+extern "C" int mla_dcp_reorganize_context(const void* gathered_k, const void* gathered_v, int32_t num_heads,
+                                          int32_t world_size, int32_t interleave, int32_t local_rows,
+                                          const int32_t* entry_starts, const int32_t* entry_row_offsets,
+                                          const int32_t* entry_local_offsets, int32_t num_entries,
+                                          int32_t num_rows, void* ws_k, void* ws_v, void* stream) {
+    if (num_heads < 1 || world_size < 1 || interleave < 1 || local_rows < 0 || num_entries < 0 || num_rows < 0)
+        return MLA_ERR_INVALID_ARG;
+    if (num_rows == 0) return MLA_OK;
+    if (num_entries == 0 || gathered_k == nullptr || gathered_v == nullptr || entry_starts == nullptr ||
+        entry_row_offsets == nullptr || entry_local_offsets == nullptr || ws_k == nullptr || ws_v == nullptr)
+        return MLA_ERR_INVALID_ARG;
+    if (!mla::aligned16(gathered_k) || !mla::aligned16(gathered_v) || !mla::aligned16(ws_k) ||
+        !mla::aligned16(ws_v))
+        return MLA_ERR_INVALID_ARG;
+    return mla::launch_dcp_reorganize(static_cast<const mla::bf16_t*>(gathered_k),
+                                      static_cast<const mla::bf16_t*>(gathered_v), num_heads, world_size, interleave,
+                                      local_rows, entry_starts, entry_row_offsets, entry_local_offsets, num_entries,
+                                      num_rows, static_cast<mla::bf16_t*>(ws_k), static_cast<mla::bf16_t*>(ws_v),
+                                      static_cast<hipStream_t>(stream));
 }

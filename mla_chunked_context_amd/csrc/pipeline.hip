@@ -16,6 +16,11 @@
 // A single chunk that covers every token (the digest's early exit when one
 // chunk covers all context) needs neither the init nor any accumulate: its
 // attention output is the partial.
+//
+// Two more drivers share the pieces: the same loop with each chunk's rows
+// assembled as under DCP (local gathers into the all-gather layout, then a
+// reorganisation into request order), and the uniform-window scheduler that
+// per-request packing replaced.
 #include <algorithm>
 #include <array>
 #include <cstring>
@@ -49,13 +54,16 @@ struct VecSink : PlanSink {
     int32_t entries_so_far() const override { return static_cast<int32_t>(p->starts.size()); }
 };
 
-// Device metadata of one chunk, as offsets (in int32 elements) into the meta block.
+// Device metadata of one chunk, as offsets (in int32 elements) into the meta
+// block.  e_lstart / e_loff (local starts and offsets) exist only under DCP.
 struct ChunkMeta {
-    int64_t e_req, e_start, e_off, cu_q;
+    int64_t e_req, e_start, e_off, cu_q, e_lstart = 0, e_loff = 0;
+    int32_t rows = 0;        // context rows (request order)
+    int32_t local_rows = 0;  // padded local rows of one rank (DCP)
 };
 
 struct Layout {
-    int64_t ws_k, ws_v, part_out, part_lse, suf_out, suf_lse, tmp_out, tmp_lse, meta;
+    int64_t ws_k, ws_v, part_out, part_lse, suf_out, suf_lse, tmp_out, tmp_lse, meta, g_k = 0, g_v = 0;
     int64_t total;
     int64_t tmp_rows;   // rows of the continuation temporary
     int64_t meta_ints;  // int32 elements of metadata
@@ -70,15 +78,19 @@ struct Problem {
     int32_t max_q = 0;
     int64_t prefix_num_tokens = 0;
     std::vector<int32_t> empty;  // pairs
+    int32_t world = 1, interleave = 1;
     Layout lay{};
 };
 
-int build_problem(const mla_chunked_prefill_params& p, Problem& pb) {
+int build_problem(const mla_chunked_prefill_params& p, Problem& pb, bool dcp = false, int32_t world = 1,
+                  int32_t interleave = 1) {
     const int32_t n = p.num_requests;
     VecSink sink;
     sink.p = &pb.plan;
+    pb.world = world;
+    pb.interleave = interleave;
     int st = plan_chunks(p.context_lens, p.query_lens, n, p.workspace_rows, p.max_context_chunk, p.split_alignment,
-                         sink);
+                         sink, world, interleave);
     if (st != MLA_OK) return st;
     int32_t n_empty = 0;
     st = token_info(p.context_lens, p.query_lens, n, &pb.prefix_num_tokens, nullptr, 0, &n_empty);
@@ -110,9 +122,23 @@ int build_problem(const mla_chunked_prefill_params& p, Problem& pb) {
             off += pb.plan.lens[c.entry_begin + i];
             pb.meta.push_back(off);
         }
+        m.rows = off;
         m.cu_q = static_cast<int64_t>(pb.meta.size());
         for (int32_t i = 0; i <= ne; ++i)
             pb.meta.push_back(static_cast<int32_t>(qsl[c.request_begin + i] - qsl[c.request_begin]));
+        if (dcp) {
+            m.e_lstart = static_cast<int64_t>(pb.meta.size());
+            for (int32_t i = 0; i < ne; ++i) pb.meta.push_back(pb.plan.starts[c.entry_begin + i] / world);
+            m.e_loff = static_cast<int64_t>(pb.meta.size());
+            int64_t loff = 0;
+            pb.meta.push_back(0);
+            for (int32_t i = 0; i < ne; ++i) {
+                const int64_t s0 = pb.plan.starts[c.entry_begin + i], len = pb.plan.lens[c.entry_begin + i];
+                loff += padded_local_rows(s0 + len, world, interleave) - s0 / world;
+                pb.meta.push_back(static_cast<int32_t>(loff));
+            }
+            m.local_rows = static_cast<int32_t>(loff);
+        }
         pb.cmeta.push_back(m);
         if (c.is_continuation) tmp_rows = std::max<int64_t>(tmp_rows, p.query_lens[c.request_begin]);
     }
@@ -139,6 +165,12 @@ int build_problem(const mla_chunked_prefill_params& p, Problem& pb) {
     L.tmp_lse = take(H * tmp_rows * 4);
     L.meta_ints = static_cast<int64_t>(pb.meta.size());
     L.meta = take(L.meta_ints * 4);
+    if (dcp) {
+        int64_t g_rows = 0;
+        for (const auto& m : pb.cmeta) g_rows = std::max<int64_t>(g_rows, static_cast<int64_t>(world) * m.local_rows);
+        L.g_k = take(g_rows * H * kDk * 2);
+        L.g_v = take(g_rows * H * kDv * 2);
+    }
     L.total = o;
     return MLA_OK;
 }
@@ -297,33 +329,12 @@ int check_buffers(const mla_chunked_prefill_params& p, bool needs_cache, int64_t
     return MLA_OK;
 }
 
-}  // namespace
-
-}  // namespace mla
-
-extern "C" {
-
-int mla_chunked_prefill_scratch_size(const mla_chunked_prefill_params* params, int64_t* bytes) {
-    if (bytes == nullptr) return MLA_ERR_INVALID_ARG;
-    MLA_TRY(mla::check_params(params));
-    mla::Problem pb;
-    MLA_TRY(mla::build_problem(*params, pb));
-    *bytes = pb.lay.total;
-    return MLA_OK;
-}
-
-int mla_chunked_prefill(const mla_chunked_prefill_params* params, void* stream_v) {
-    using namespace mla;
-    MLA_TRY(check_params(params));
-    const mla_chunked_prefill_params& p = *params;
-    Problem pb;
-    MLA_TRY(build_problem(p, pb));
+// The chunk loop shared by the single-device and DCP drivers: `gather`
+// fills the workspace with a chunk's context rows in request order.
+template <class Gather>
+int run_chunked(const mla_chunked_prefill_params& p, const Problem& pb, hipStream_t stream, Gather gather) {
     const int64_t T = pb.tokens;
     const int32_t H = p.num_heads;
-    if (T == 0) return MLA_OK;
-    MLA_TRY(check_buffers(p, !pb.plan.chunks.empty(), pb.lay.total));
-
-    hipStream_t stream = static_cast<hipStream_t>(stream_v);
     char* base = static_cast<char*>(p.scratch);
     const Layout& L = pb.lay;
     bf16_t* ws_k = reinterpret_cast<bf16_t*>(base + L.ws_k);
@@ -351,9 +362,7 @@ int mla_chunked_prefill(const mla_chunked_prefill_params* params, void* stream_v
     for (size_t ci = 0; ci < pb.plan.chunks.size(); ++ci) {
         const mla_chunk_desc& c = pb.plan.chunks[ci];
         const ChunkMeta& m = pb.cmeta[ci];
-        MLA_TRY(launch_gather(static_cast<const bf16_t*>(p.k_cache), static_cast<const bf16_t*>(p.v_cache),
-                              p.num_blocks, p.block_size, H, p.block_table, p.block_table_width, meta + m.e_req,
-                              meta + m.e_start, meta + m.e_off, c.num_entries, c.num_rows, ws_k, ws_v, stream));
+        MLA_TRY(gather(c, m, meta, ws_k, ws_v, stream));
         const bf16_t* qc = q + c.token_begin * qrow;
         bf16_t* pc = part_out + c.token_begin * orow;
         float* lc = part_lse + c.token_begin;
@@ -381,6 +390,92 @@ int mla_chunked_prefill(const mla_chunked_prefill_params* params, void* stream_v
     MLA_TRY(launch_merge(static_cast<bf16_t*>(p.out), p.out_lse, part_out, part_lse, suf_out, suf_lse, T, H, kDv,
                          T, T, T, pb.prefix_num_tokens, stream));
     return MLA_OK;
+}
+
+}  // namespace
+
+}  // namespace mla
+
+extern "C" {
+
+int mla_chunked_prefill_scratch_size(const mla_chunked_prefill_params* params, int64_t* bytes) {
+    if (bytes == nullptr) return MLA_ERR_INVALID_ARG;
+    MLA_TRY(mla::check_params(params));
+    mla::Problem pb;
+    MLA_TRY(mla::build_problem(*params, pb));
+    *bytes = pb.lay.total;
+    return MLA_OK;
+}
+
+int mla_chunked_prefill(const mla_chunked_prefill_params* params, void* stream_v) {
+    using namespace mla;
+    MLA_TRY(check_params(params));
+    const mla_chunked_prefill_params& p = *params;
+    Problem pb;
+    MLA_TRY(build_problem(p, pb));
+    if (pb.tokens == 0) return MLA_OK;
+    MLA_TRY(check_buffers(p, !pb.plan.chunks.empty(), pb.lay.total));
+    const int32_t H = p.num_heads;
+    auto gather = [&](const mla_chunk_desc& c, const ChunkMeta& m, const int32_t* meta, bf16_t* ws_k, bf16_t* ws_v,
+                      hipStream_t stream) {
+        return launch_gather(static_cast<const bf16_t*>(p.k_cache), static_cast<const bf16_t*>(p.v_cache),
+                             p.num_blocks, p.block_size, H, p.block_table, p.block_table_width, meta + m.e_req,
+                             meta + m.e_start, meta + m.e_off, c.num_entries, m.rows, ws_k, ws_v, stream);
+    };
+    return run_chunked(p, pb, static_cast<hipStream_t>(stream_v), gather);
+}
+
+int mla_dcp_chunked_prefill_scratch_size(const mla_chunked_prefill_params* params, const mla_dcp_ranks* ranks,
+                                         int64_t* bytes) {
+    if (bytes == nullptr || ranks == nullptr) return MLA_ERR_INVALID_ARG;
+    MLA_TRY(mla::check_params(params));
+    mla::Problem pb;
+    MLA_TRY(mla::build_problem(*params, pb, true, ranks->world_size, ranks->interleave));
+    *bytes = pb.lay.total;
+    return MLA_OK;
+}
+
+int mla_dcp_chunked_prefill(const mla_chunked_prefill_params* params, const mla_dcp_ranks* ranks, void* stream_v) {
+    using namespace mla;
+    MLA_TRY(check_params(params));
+    if (ranks == nullptr || ranks->world_size < 1 || ranks->interleave < 1) return MLA_ERR_INVALID_ARG;
+    const mla_chunked_prefill_params& p = *params;
+    const int32_t D = ranks->world_size;
+    Problem pb;
+    MLA_TRY(build_problem(p, pb, true, D, ranks->interleave));
+    if (pb.tokens == 0) return MLA_OK;
+    MLA_TRY(check_buffers(p, false, pb.lay.total));
+    if (!pb.plan.chunks.empty()) {
+        if (ranks->k_cache == nullptr || ranks->v_cache == nullptr || ranks->block_table == nullptr ||
+            ranks->num_blocks == nullptr || ranks->block_table_width == nullptr)
+            return MLA_ERR_INVALID_ARG;
+        for (int32_t r = 0; r < D; ++r) {
+            if (ranks->k_cache[r] == nullptr || ranks->v_cache[r] == nullptr || ranks->block_table[r] == nullptr ||
+                !aligned16(ranks->k_cache[r]) || !aligned16(ranks->v_cache[r]) || ranks->num_blocks[r] < 0 ||
+                ranks->block_table_width[r] < 0)
+                return MLA_ERR_INVALID_ARG;
+        }
+    }
+    const int32_t H = p.num_heads;
+    char* base = static_cast<char*>(p.scratch);
+    bf16_t* g_k = reinterpret_cast<bf16_t*>(base + pb.lay.g_k);
+    bf16_t* g_v = reinterpret_cast<bf16_t*>(base + pb.lay.g_v);
+    const int64_t krow = static_cast<int64_t>(H) * kDk, vrow = static_cast<int64_t>(H) * kDv;
+    auto gather = [&](const mla_chunk_desc& c, const ChunkMeta& m, const int32_t* meta, bf16_t* ws_k, bf16_t* ws_v,
+                      hipStream_t stream) {
+        // each rank's padded local rows go where an all-gather would put them
+        for (int32_t r = 0; r < D; ++r) {
+            const int64_t at = static_cast<int64_t>(r) * m.local_rows;
+            MLA_TRY(launch_gather(static_cast<const bf16_t*>(ranks->k_cache[r]),
+                                  static_cast<const bf16_t*>(ranks->v_cache[r]), ranks->num_blocks[r], p.block_size,
+                                  H, ranks->block_table[r], ranks->block_table_width[r], meta + m.e_req,
+                                  meta + m.e_lstart, meta + m.e_loff, c.num_entries, m.local_rows, g_k + at * krow,
+                                  g_v + at * vrow, stream));
+        }
+        return launch_dcp_reorganize(g_k, g_v, H, D, ranks->interleave, m.local_rows, meta + m.e_start,
+                                     meta + m.e_off, meta + m.e_loff, c.num_entries, m.rows, ws_k, ws_v, stream);
+    };
+    return run_chunked(p, pb, static_cast<hipStream_t>(stream_v), gather);
 }
 
 }  // extern "C"

@@ -30,8 +30,12 @@ int64_t aligned_head(int64_t rest, int64_t room, int64_t cap, int64_t align) {
 }  // namespace
 
 int plan_chunks(const int32_t* ctx, const int32_t* qlens, int32_t n, int64_t budget, int64_t cap,
-                int32_t align, PlanSink& sink) {
+                int32_t align, PlanSink& sink, int32_t world, int32_t interleave) {
     if (n < 0 || align < 1 || budget < align) return MLA_ERR_INVALID_ARG;
+    if (world < 1 || interleave < 1 || align % (static_cast<int64_t>(world) * interleave) != 0)
+        return MLA_ERR_INVALID_ARG;
+    // workspace rows of context positions [0, x): identity on one device
+    auto padded = [&](int64_t x) { return world * padded_local_rows(x, world, interleave); };
     if (cap <= 0) cap = budget;
     if (cap < align) return MLA_ERR_INVALID_ARG;
     if (n > 0 && (ctx == nullptr || qlens == nullptr)) return MLA_ERR_INVALID_ARG;
@@ -79,10 +83,12 @@ int plan_chunks(const int32_t* ctx, const int32_t* qlens, int32_t n, int64_t bud
             const int64_t room = budget - rows;
             int64_t take;
             bool full;
-            if (rest <= room) {
+            if (padded(c) - padded(pos) <= room) {
                 take = rest;
                 full = false;
             } else {
+                // pos and every candidate head are multiples of align, hence of
+                // world * interleave, so a head's rows equal its length
                 take = aligned_head(rest, room, cap, align);
                 full = true;  // nothing more goes into this chunk
             }
@@ -92,7 +98,7 @@ int plan_chunks(const int32_t* ctx, const int32_t* qlens, int32_t n, int64_t bud
                 cur.num_entries += 1;
                 cur.max_seq_len = std::max<int32_t>(cur.max_seq_len, static_cast<int32_t>(take));
                 cur.max_query_len = std::max<int32_t>(cur.max_query_len, qlens[r]);
-                rows += take;
+                rows += padded(pos + take) - padded(pos);
                 pos += take;
             }
             if (full) {
@@ -225,6 +231,39 @@ int mla_plan_context_chunks(const int32_t* context_lens, const int32_t* query_le
     *num_chunks = sink.n_chunks;
     *num_entries = sink.n_entries;
     if (sink.n_chunks > chunk_capacity || sink.n_entries > entry_capacity) return MLA_ERR_CAPACITY;
+    return MLA_OK;
+}
+
+int mla_plan_dcp_context_chunks(const int32_t* context_lens, const int32_t* query_lens, int32_t num_requests,
+                                int64_t row_budget, int64_t max_context_chunk, int32_t split_alignment,
+                                int32_t world_size, int32_t interleave, mla_chunk_desc* chunks,
+                                int32_t chunk_capacity, int32_t* num_chunks, int32_t* entry_starts,
+                                int32_t* entry_seq_lens, int32_t* entry_local_starts, int32_t* entry_local_lens,
+                                int32_t entry_capacity, int32_t* num_entries) {
+    if (num_chunks == nullptr || num_entries == nullptr) return MLA_ERR_INVALID_ARG;
+    if (chunk_capacity < 0 || entry_capacity < 0) return MLA_ERR_INVALID_ARG;
+    if ((chunk_capacity > 0 && chunks == nullptr) ||
+        (entry_capacity > 0 && (entry_starts == nullptr || entry_seq_lens == nullptr ||
+                                entry_local_starts == nullptr || entry_local_lens == nullptr)))
+        return MLA_ERR_INVALID_ARG;
+    ArraySink sink;
+    sink.chunks = chunks;
+    sink.chunk_cap = chunk_capacity;
+    sink.starts = entry_starts;
+    sink.lens = entry_seq_lens;
+    sink.entry_cap = entry_capacity;
+    const int st = mla::plan_chunks(context_lens, query_lens, num_requests, row_budget, max_context_chunk,
+                                    split_alignment, sink, world_size, interleave);
+    if (st != MLA_OK) return st;
+    *num_chunks = sink.n_chunks;
+    *num_entries = sink.n_entries;
+    if (sink.n_chunks > chunk_capacity || sink.n_entries > entry_capacity) return MLA_ERR_CAPACITY;
+    for (int32_t e = 0; e < sink.n_entries; ++e) {
+        const int64_t s = entry_starts[e], len = entry_seq_lens[e];
+        entry_local_starts[e] = static_cast<int32_t>(s / world_size);
+        entry_local_lens[e] =
+            static_cast<int32_t>(mla::padded_local_rows(s + len, world_size, interleave) - s / world_size);
+    }
     return MLA_OK;
 }
 

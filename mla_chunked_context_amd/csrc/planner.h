@@ -18,8 +18,18 @@ struct PlanSink {
 };
 
 // Greedy aligned packing; returns an MLA_* status.  cap <= 0 means budget.
+// world/interleave > 1: context sharded over `world` ranks in runs of
+// `interleave` positions; a chunk's rows are then counted in the all-gathered
+// workspace, padded_rows(x) = world * interleave * ceil(x / (world * interleave)),
+// and align must be a multiple of world * interleave.
 int plan_chunks(const int32_t* ctx, const int32_t* qlens, int32_t n, int64_t budget, int64_t cap,
-                int32_t align, PlanSink& sink);
+                int32_t align, PlanSink& sink, int32_t world = 1, int32_t interleave = 1);
+
+// Rows every rank reserves for context positions [0, x) under that sharding.
+inline int64_t padded_local_rows(int64_t x, int32_t world, int32_t interleave) {
+    const int64_t round = static_cast<int64_t>(world) * interleave;
+    return (x + round - 1) / round * interleave;
+}
 
 // prefill_tokens_with_context and the token ranges of requests without context.
 int token_info(const int32_t* ctx, const int32_t* qlens, int32_t n, int64_t* prefix_num_tokens,

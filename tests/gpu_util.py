@@ -89,13 +89,14 @@ def context_rows(b, r, heads):
     return host(k), host(v)
 
 
-def sampled_check(mla, wl, tokens_per_request=6, seed=0, path="chunked", device="cuda:0"):
+def sampled_check(mla, wl, tokens_per_request=6, seed=0, path="chunked", device="cuda:0", runner=None):
     """Full-size run of a workload, checked on sampled rows (first, last,
     middle and random tokens of each request; a few heads) against the direct
-    definition computed one row at a time, plus no-NaN / finite-LSE everywhere."""
+    definition computed one row at a time, plus no-NaN / finite-LSE everywhere.
+    ``runner(batch) -> (out, lse)`` replaces run_prefill when given."""
     say(f"{path} full size {wl.name}: N={wl.num_requests} T={wl.num_tokens} ctx={sum(wl.context_lens)}")
     b = W.make_batch(wl, device=device, canary=False)
-    out, lse = run_prefill(mla, b, path=path)
+    out, lse = runner(b) if runner is not None else run_prefill(mla, b, path=path)
     say("  ran; checking")
     assert not torch.isnan(out).any().item() and torch.isfinite(lse).all().item()
     rng = np.random.default_rng(seed)

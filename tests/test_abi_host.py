@@ -233,3 +233,51 @@ def test_uniform_window_prefill_host_checks():
     p.workspace_rows = n_ctx * 64 - 1  # below one aligned window per request
     with pytest.raises(mla.MlaError):
         mla.mla_uniform_window_prefill_scratch_size(p)
+
+
+def test_dcp_planner_matches_oracle():
+    import oracle.dcp as OD
+    rng = np.random.default_rng(12)
+    cases = [(1, 1), (2, 1), (4, 1), (8, 1), (2, 4), (4, 2), (3, 1)]
+    for _ in range(1500):
+        world, il = cases[int(rng.integers(0, len(cases)))]
+        a = world * il * int(rng.choice([1, 2, 8]))
+        n = int(rng.integers(1, 12))
+        ctx = [0 if rng.random() < 0.2 else int(rng.integers(1, 5000)) for _ in range(n)]
+        ql = [int(rng.integers(0, 50)) for _ in range(n)]
+        w = int(rng.integers(a, 6000))
+        chunks, st, ln, lst, lln = mla.mla_plan_dcp_context_chunks(ctx, ql, w, world, il, 0, a)
+        plans = OD.plan_dcp_context_chunks(ctx, w, a, world, il)
+        assert len(chunks) == len(plans)
+        for c, pl in zip(chunks, plans):
+            e0, e1 = c["entry_begin"], c["entry_begin"] + c["num_entries"]
+            ls, lens, cu = OD.dcp_local_entries(pl, world, il)
+            assert (c["request_begin"], c["request_end"]) == (pl.request_start, pl.request_end)
+            assert list(st[e0:e1]) == pl.starts and list(ln[e0:e1]) == pl.seq_lens
+            assert list(lst[e0:e1]) == ls and list(lln[e0:e1]) == lens
+            assert c["num_rows"] == world * int(cu[-1])
+    with pytest.raises(mla.MlaError):
+        mla.mla_plan_dcp_context_chunks([100], [1], 256, 4, 8, 0, 16)  # 16 is not a multiple of 32
+
+
+def test_dcp_entry_points_reject_bad_arguments_without_gpu():
+    f = mla._lib
+    assert f.mla_dcp_reorganize_context(None, None, 0, 2, 1, 4, None, None, None, 1, 4, None, None, None) == 1
+    assert f.mla_dcp_reorganize_context(None, None, 2, 2, 1, 4, None, None, None, 1, 0, None, None, None) == 0
+    wl = W.named_workloads()[1]
+    p = mla.ChunkedPrefillParams()
+    ctx = np.asarray(wl.context_lens, dtype=np.int32)
+    ql = np.asarray(wl.query_lens, dtype=np.int32)
+    p.context_lens, p.query_lens, p.num_requests = ctx.ctypes.data, ql.ctypes.data, len(ctx)
+    p.num_heads, p.block_size = wl.num_heads, wl.block_size
+    p.scale, p.workspace_rows, p.split_alignment = wl.scale, wl.workspace_rows, 64
+    ranks = mla.DcpRanks()
+    ranks.world_size, ranks.interleave = 4, 1
+    n = mla.mla_dcp_chunked_prefill_scratch_size(p, ranks)
+    assert n >= mla.mla_chunked_prefill_scratch_size(p)
+    p.scratch_bytes = n
+    with pytest.raises(mla.MlaError):  # null device pointers
+        mla.mla_dcp_chunked_prefill(p, ranks, stream=0)
+    ranks.world_size = 3  # 64 is not a multiple of 3
+    with pytest.raises(mla.MlaError):
+        mla.mla_dcp_chunked_prefill_scratch_size(p, ranks)

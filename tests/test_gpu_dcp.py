@@ -1,0 +1,139 @@
+"""GPU parity of the DCP pieces against the oracle, through the C ABI.
+
+* mla_dcp_reorganize_context: per-rank local gathers (mla_gather_context on
+  each rank's cache, written where an all-gather would put them), then the
+  reorganisation, must equal the oracle's gather of the unsharded cache bit
+  for bit, for every chunk of the plan;
+* mla_dcp_chunked_prefill: every row and LSE against the oracle's DCP path on
+  small and random batches, and sampled rows against the direct definition on
+  the homogeneous batch sharded over 4 ranks.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import oracle.dcp as OD
+import workloads as W
+from tests.gpu_util import check, host, sampled_check, say
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+import mla_chunked_context_amd as mla  # noqa: E402
+
+DEV = "cuda:0"
+SMALL = W.Workload("dcp_small", (768, 300, 0, 515, 64), (3, 5, 2, 4, 1), 2, 512, 64, 16, 1.0, 8)
+
+
+def _i32(x):
+    return torch.tensor(np.asarray(x, dtype=np.int32), device=DEV)
+
+
+@pytest.mark.parametrize("world,il", [(2, 1), (4, 1), (2, 4), (8, 2)])
+def test_reorganize_equals_single_device_gather(world, il):
+    wl = SMALL
+    say(f"dcp reorganize world={world} interleave={il}")
+    b = W.make_batch(wl, device="cpu", canary=True)
+    ranks = W.shard_context(b, world, il)
+    dranks = [W.RankCache(r.k_cache.to(DEV), r.v_cache.to(DEV), r.block_table.to(DEV), r.num_blocks, r.context_lens)
+              for r in ranks]
+    chunks, st, ln, lst, lln = mla.mla_plan_dcp_context_chunks(wl.context_lens, wl.query_lens, wl.workspace_rows,
+                                                               world, il, 0, wl.split_alignment)
+    H = wl.num_heads
+    kc, vc = W.to_f64(b.k_cache), W.to_f64(b.v_cache)
+    for c in chunks:
+        e0, ne = c["entry_begin"], c["num_entries"]
+        req = list(range(c["request_begin"], c["request_end"]))
+        lcu = np.concatenate([[0], np.cumsum(lln[e0:e0 + ne])])
+        cu = np.concatenate([[0], np.cumsum(ln[e0:e0 + ne])])
+        L = int(lcu[-1])
+        assert world * L == c["num_rows"]
+        gk = torch.full((world * L, H, W.DK), float("nan"), dtype=torch.bfloat16, device=DEV)
+        gv = torch.full((world * L, H, W.DV), float("nan"), dtype=torch.bfloat16, device=DEV)
+        for r, rc in enumerate(dranks):
+            mla.mla_gather_context(rc.k_cache, rc.v_cache, rc.block_table, _i32(req), _i32(lst[e0:e0 + ne]),
+                                   _i32(lcu), L, gk[r * L:(r + 1) * L], gv[r * L:(r + 1) * L])
+        rows = int(cu[-1])
+        wk = torch.full((rows, H, W.DK), float("nan"), dtype=torch.bfloat16, device=DEV)
+        wv = torch.full((rows, H, W.DV), float("nan"), dtype=torch.bfloat16, device=DEV)
+        mla.mla_dcp_reorganize_context(gk, gv, world, il, L, _i32(st[e0:e0 + ne]), _i32(cu), _i32(lcu), rows, wk, wv)
+        torch.cuda.synchronize()
+        ref_k = O.gather_context_rows(kc, b.block_table.numpy(), wl.block_size, req, st[e0:e0 + ne], ln[e0:e0 + ne])
+        ref_v = O.gather_context_rows(vc, b.block_table.numpy(), wl.block_size, req, st[e0:e0 + ne], ln[e0:e0 + ne])
+        assert np.array_equal(host(wk), ref_k) and np.array_equal(host(wv), ref_v)
+
+
+def _run_dcp(b, ranks, world, il):
+    wl = b.wl
+    T, H = wl.num_tokens, wl.num_heads
+    out = torch.full((T, H, W.DV), float("nan"), dtype=torch.bfloat16, device=DEV)
+    lse = torch.full((H, T), float("nan"), dtype=torch.float32, device=DEV)
+    dr = mla.make_dcp_ranks(ranks, il)
+    mk = lambda s=None: mla.make_prefill_params(  # noqa: E731
+        b.q, b.k_new, b.v_new, None, None, None, wl.context_lens, wl.query_lens, wl.workspace_rows,
+        wl.split_alignment, wl.scale, out=out, out_lse=lse, scratch=s)
+    p = mk()
+    p.block_size = wl.block_size
+    n = mla.mla_dcp_chunked_prefill_scratch_size(p, dr)
+    scratch = torch.full(((max(n, 256) + 1) // 2,), float("nan"), dtype=torch.bfloat16, device=DEV)
+    p = mk(scratch)
+    p.block_size = wl.block_size
+    mla.mla_dcp_chunked_prefill(p, dr)
+    torch.cuda.synchronize()
+    return out, lse
+
+
+@pytest.mark.parametrize("world,il", [(2, 1), (4, 1), (4, 2)])
+def test_dcp_prefill_small_full(world, il):
+    wl = SMALL
+    say(f"dcp prefill small world={world} interleave={il}")
+    b = W.make_batch(wl, device="cpu", canary=True)
+    ranks = W.shard_context(b, world, il)
+    f = W.to_f64
+    ref = OD.dcp_chunked_prefill(f(b.q), f(b.k_new), f(b.v_new), [f(r.k_cache) for r in ranks],
+                                 [f(r.v_cache) for r in ranks], [r.block_table.numpy() for r in ranks], wl.block_size,
+                                 wl.context_lens, wl.query_lens, wl.workspace_rows, wl.split_alignment, wl.scale,
+                                 world, il)
+    d = W.Batch(wl, b.q.to(DEV), b.k_new.to(DEV), b.v_new.to(DEV), b.k_cache.to(DEV), b.v_cache.to(DEV),
+                b.block_table.to(DEV), b.num_blocks, b.spare_blocks)
+    dr = [W.RankCache(r.k_cache.to(DEV), r.v_cache.to(DEV), r.block_table.to(DEV), r.num_blocks, r.context_lens)
+          for r in ranks]
+    out, lse = _run_dcp(d, dr, world, il)
+    vmax = float(max(np.abs(f(b.v_new)).max(), np.nanmax(np.abs(f(b.v_cache)))))
+    say("  ", check(host(out), lse.double().cpu().numpy(), ref["out"], ref["lse"], vmax, "dcp small"))
+
+
+def test_dcp_prefill_random_full():
+    for seed in range(8):
+        world, il = [(2, 1), (4, 1), (2, 2), (8, 1)][seed % 4]
+        wl = W.random_workload(seed, max_requests=6, max_ctx=600, max_q=60, heads=(1, 2),
+                               alignments=(world * il, 2 * world * il))
+        say(f"dcp random seed={seed} world={world} il={il} ctx={wl.context_lens} q={wl.query_lens} "
+            f"W={wl.workspace_rows} A={wl.split_alignment} B={wl.block_size}")
+        b = W.make_batch(wl, device="cpu", canary=True)
+        ranks = W.shard_context(b, world, il)
+        f = W.to_f64
+        ref = O.direct_prefill(f(b.q), f(b.k_new), f(b.v_new), f(b.k_cache), f(b.v_cache), b.block_table.numpy(),
+                               wl.block_size, wl.context_lens, wl.query_lens, wl.scale)
+        d = W.Batch(wl, b.q.to(DEV), b.k_new.to(DEV), b.v_new.to(DEV), b.k_cache.to(DEV), b.v_cache.to(DEV),
+                    b.block_table.to(DEV), b.num_blocks, b.spare_blocks)
+        dr = [W.RankCache(r.k_cache.to(DEV), r.v_cache.to(DEV), r.block_table.to(DEV), r.num_blocks,
+                          r.context_lens) for r in ranks]
+        out, lse = _run_dcp(d, dr, world, il)
+        vmax = float(max(np.abs(f(b.v_new)).max(), np.nanmax(np.abs(f(b.v_cache)))))
+        say("  ", check(host(out), lse.double().cpu().numpy(), ref[0], ref[1], vmax, f"dcp random {seed}"))
+
+
+def test_dcp_homogeneous_full_size_sampled():
+    world, il = 4, 1
+
+    def runner(b):
+        ranks = W.shard_context(b, world, il, canary=False)
+        res = _run_dcp(b, ranks, world, il)
+        del ranks
+        return res
+
+    sampled_check(mla, W.named_workloads()[3], path=f"dcp world={world}", runner=runner)

@@ -209,3 +209,56 @@ def make_batch(wl: Workload, device="cpu", gen_device=None, canary=True) -> Batc
 def to_f64(t: torch.Tensor) -> np.ndarray:
     """Exact fp64 copy of a bf16 tensor (every bf16 value is an fp64 value)."""
     return t.detach().to("cpu").to(torch.float64).numpy()
+
+
+# ----------------------------------------------------------------------------
+# context sharded over emulated ranks
+
+
+@dataclass
+class RankCache:
+    """One rank's share of the paged context cache (its positions, in order)."""
+
+    k_cache: torch.Tensor
+    v_cache: torch.Tensor
+    block_table: torch.Tensor
+    num_blocks: int
+    context_lens: list
+
+
+def shard_context(b: Batch, world: int, interleave: int = 1, canary=True, seed: int = 0):
+    """Split ``b``'s paged cache over ``world`` ranks: runs of ``interleave``
+    consecutive context positions go to ranks in turn (run k to rank k % world),
+    and each rank stores its positions of a request in order in blocks of its
+    own (taken from a seeded permutation, with spare NaN blocks that table
+    padding points at).  Returns a list of RankCache on b's device."""
+    wl = b.wl
+    B = wl.block_size
+    dev = b.k_cache.device
+    table = b.block_table.cpu().numpy()
+    ranks = []
+    for rank in range(world):
+        positions = []
+        for r, c in enumerate(wl.context_lens):
+            p = np.arange(int(c), dtype=np.int64)
+            positions.append(p[(p // interleave) % world == rank])
+        lens = [len(p) for p in positions]
+        ltable, pool, spare = block_table_for(lens, B, 1000 * (seed + 1) + 31 * rank + world)
+        k = torch.full((pool, B) + tuple(b.k_cache.shape[2:]), float("nan") if canary else 0.0,
+                       dtype=b.k_cache.dtype, device=dev)
+        v = torch.full((pool, B) + tuple(b.v_cache.shape[2:]), float("nan") if canary else 0.0,
+                       dtype=b.v_cache.dtype, device=dev)
+        src, dst = [], []
+        for r, p in enumerate(positions):
+            if len(p) == 0:
+                continue
+            src.append(table[r][p // B].astype(np.int64) * B + p % B)
+            li = np.arange(len(p), dtype=np.int64)
+            dst.append(ltable[r][li // B].astype(np.int64) * B + li % B)
+        if src:
+            s = torch.from_numpy(np.concatenate(src)).to(dev)
+            d = torch.from_numpy(np.concatenate(dst)).to(dev)
+            k.view(pool * B, -1).index_copy_(0, d, b.k_cache.view(-1, k.shape[2] * k.shape[3]).index_select(0, s))
+            v.view(pool * B, -1).index_copy_(0, d, b.v_cache.view(-1, v.shape[2] * v.shape[3]).index_select(0, s))
+        ranks.append(RankCache(k, v, torch.from_numpy(ltable).to(dev), pool, lens))
+    return ranks

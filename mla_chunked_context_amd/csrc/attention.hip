@@ -175,8 +175,10 @@ __device__ __forceinline__ void attention_body(const AttnArgs& a, unsigned char*
     const int32_t k_row_bytes = H * kDk * 2;
     const int32_t v_row_bytes = H * kDv * 2;
     // K tile in LDS: row r (key) holds its 24 16-byte chunks with chunk c at
-    // position c ^ (r & 7), so that the 32 rows read by one MFMA operand load
-    // hit distinct banks without padding.  Each wave fills 3 KB of the tile
+    // position c ^ ((r >> 1) & 7).  Rows are 384 bytes, so rows of equal parity
+    // start on the same bank; the swizzle gives the 16 rows that an MFMA
+    // operand load serves together 16 distinct 16-byte bank groups (no
+    // conflicts, no padding).  Each wave fills 3 KB of the tile
     // with direct-to-LDS loads (lane l writes 16 bytes at l * 16); the lane
     // picks the global chunk that belongs at that LDS position.
     int32_t k_goff[kKLoads];
@@ -184,7 +186,7 @@ __device__ __forceinline__ void attention_body(const AttnArgs& a, unsigned char*
     for (int i = 0; i < kKLoads; ++i) {
         const int pbyte = (wave * kKLoads + i) * 1024 + lane * 16;
         const int row = pbyte / kKRowBytes;
-        const int chunk = ((pbyte % kKRowBytes) >> 4) ^ (row & 7);
+        const int chunk = ((pbyte % kKRowBytes) >> 4) ^ ((row >> 1) & 7);
         k_goff[i] = row * k_row_bytes + chunk * 16;
     }
     const int vkp = tid & 31;  // keys 2*vkp, 2*vkp+1 of the tile
@@ -230,10 +232,10 @@ __device__ __forceinline__ void attention_body(const AttnArgs& a, unsigned char*
     const int32_t wave_last_q = wave_first_q + kQPerWave - 1;
     // per-lane LDS bases; every fragment read is base + a compile-time offset
     // per-lane K fragment addresses for the four values of ks & 3
-    // (chunk 2*ks + g sits at (2*ks + g) ^ (l32 & 7) in row kb*32 + l32)
+    // (chunk 2*ks + g sits at (2*ks + g) ^ ((l32 >> 1) & 7) in row kb*32 + l32)
     const unsigned char* k_lane[4];
 #pragma unroll
-    for (int m = 0; m < 4; ++m) k_lane[m] = k_lds + l32 * kKRowBytes + (((2 * m + g) ^ (l32 & 7)) << 4);
+    for (int m = 0; m < 4; ++m) k_lane[m] = k_lds + l32 * kKRowBytes + (((2 * m + g) ^ ((l32 >> 1) & 7)) << 4);
     const bf16_t* v_lane = vt_lds + l32 * kVtStride + g * 8;
 
     // S^T = K Q^T of one tile, from K buffer `kbuf` (compile-time)
@@ -266,16 +268,18 @@ __device__ __forceinline__ void attention_body(const AttnArgs& a, unsigned char*
     // O += V(j) P(j) (each P fragment is produced just before the MFMAs that
     // consume it), then issues the MFMAs of S(j+1), whose results are only
     // needed after the barrier.
-    // LDS: K runs one tile ahead of V, each in a ring of two buffers; at the
-    // end of iteration j, K(j+2) overwrites K(j) (last read in iteration j-1)
-    // and V(j+1) overwrites V(j-1) (also last read in iteration j-1), then one
-    // barrier publishes them.
+    // LDS: K runs one tile ahead of V, each in a ring of two buffers.  Iteration
+    // j starts by storing V(j+1) (loaded into registers during iteration j-1)
+    // over V(j-1), then issues K(j+2) straight into K(j)'s buffer and the
+    // register loads of V(j+2); both buffers were last read in iteration j-1.
+    // The barrier at the end of the iteration publishes them.
     f32x16 s_cur[2], s_nxt[2];
     if (n_tiles > 0) {
         load_k(0, 0);
         if (n_tiles > 1) load_k(kBlockN, 1);
         load_v(0);
         store_v(0);
+        if (n_tiles > 1) load_v(kBlockN);  // V(1): stored at the start of iteration 0
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // direct-to-LDS loads have landed
     __syncthreads();
@@ -285,10 +289,13 @@ __device__ __forceinline__ void attention_body(const AttnArgs& a, unsigned char*
     auto step = [&](int32_t j, auto par_tag) {
         constexpr int par = decltype(par_tag)::value;  // j & 1
         const int32_t k0 = j * kBlockN;
-        // K(j+2) goes straight into the buffer that held K(j), last read in
-        // iteration j-1 (before the previous barrier)
-        if (j + 2 < n_tiles) load_k(k0 + 2 * kBlockN, par);
-        if (j + 1 < n_tiles) load_v(k0 + kBlockN);
+        // V(j+1) over V(j-1); K(j+2) straight into the buffer that held K(j).
+        // Both were last read in iteration j-1, before the previous barrier.
+        if (j + 1 < n_tiles) store_v(par ^ 1);
+        if (j + 2 < n_tiles) {
+            load_k(k0 + 2 * kBlockN, par);
+            load_v(k0 + 2 * kBlockN);  // stored at the start of iteration j+1
+        }
         const bool active = !kCausal || k0 <= wave_last_q;  // a causal wave past this tile skips it
 
         // ---- mask keys of S(j) past the end (and above the diagonal when causal)
@@ -372,10 +379,10 @@ __device__ __forceinline__ void attention_body(const AttnArgs& a, unsigned char*
         // softmax and O update of tile j first; the MFMAs of S(j+1) then run
         // while the wave moves on to the end-of-tile wait and barrier
         softmax_pv();
-        if (j + 1 < n_tiles) store_v(par ^ 1);  // V(j-1)'s buffer: last read in iteration j-1
         scores_next();
 
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // K(j+2) has landed in LDS
+        // K(j+2) has landed in LDS (the barrier's fence also drains V(j+2))
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) s_cur[kb] = s_nxt[kb];

@@ -3,6 +3,7 @@
 //   * merge_attn_states (LSE-weighted merge, threshold copy, empty-state select),
 //   * gather of a chunk's context rows out of the paged KV cache.
 // All move 16-byte vectors; consecutive lanes touch consecutive vectors.
+#include <algorithm>
 #include <cmath>
 
 #include "device.h"
@@ -171,8 +172,15 @@ __global__ __launch_bounds__(kThreads) void merge_kernel_generic(MergeArgs a) {
 
 // ---------------------------------------------------------------- gather
 
-constexpr int kGatherRows = 4;   // workspace rows per block
-constexpr int kGatherBatch = 8;  // 16-byte vectors in flight per lane (K and V of a row together)
+constexpr int kGatherThreads = 512;  // one workspace row (H = 128: 80 KB) per block
+constexpr int kGatherBatch = 16;     // 16-byte vectors in flight per lane (K and V of a row together)
+
+// Rows per block: one row when a row fills the block's loads (H >= 52),
+// more for small head counts so that every block still moves a few KB.
+inline int32_t gather_rows_per_block(int32_t heads) {
+    const int32_t row_vectors = heads * (kDk + kDv) / 8;
+    return std::max<int32_t>(1, kGatherThreads * 8 / row_vectors);
+}
 
 // Copy of one workspace row (its K vectors, then its V vectors, as one
 // sequence of kvec + vvec 16-byte vectors): every lane issues up to
@@ -183,17 +191,17 @@ __device__ __forceinline__ void copy_row(const uint4* __restrict__ ksrc, const u
                                          bool ok) {
     const uint4 nan4 = make_uint4(0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u);
     const int n = kvec + vvec;
-    for (int base = threadIdx.x; base < n; base += kThreads * kGatherBatch) {
+    for (int base = threadIdx.x; base < n; base += kGatherThreads * kGatherBatch) {
         uint4 r[kGatherBatch];
 #pragma unroll
         for (int u = 0; u < kGatherBatch; ++u) {
-            const int v = base + u * kThreads;
+            const int v = base + u * kGatherThreads;
             r[u] = nan4;
             if (ok && v < n) r[u] = v < kvec ? load_nt(&ksrc[v]) : load_nt(&vsrc[v - kvec]);
         }
 #pragma unroll
         for (int u = 0; u < kGatherBatch; ++u) {
-            const int v = base + u * kThreads;
+            const int v = base + u * kGatherThreads;
             if (v < n) {
                 const u32x4_t val = {r[u].x, r[u].y, r[u].z, r[u].w};
                 if (v < kvec)
@@ -205,12 +213,12 @@ __device__ __forceinline__ void copy_row(const uint4* __restrict__ ksrc, const u
     }
 }
 
-__global__ __launch_bounds__(kThreads) void gather_kernel(
+__global__ __launch_bounds__(kGatherThreads) void gather_kernel(
     const uint4* __restrict__ k_cache, const uint4* __restrict__ v_cache, int64_t num_blocks, int32_t block_size,
     int32_t heads, const int32_t* __restrict__ block_table, int32_t bt_width, const int32_t* __restrict__ e_req,
     const int32_t* __restrict__ e_start, const int32_t* __restrict__ e_off, int32_t n_entries, int32_t num_rows,
-    uint4* __restrict__ ws_k, uint4* __restrict__ ws_v) {
-    const int32_t row0 = blockIdx.x * kGatherRows;
+    int32_t rows_per_block, uint4* __restrict__ ws_k, uint4* __restrict__ ws_v) {
+    const int32_t row0 = blockIdx.x * rows_per_block;
     if (row0 >= num_rows) return;
     // entry owning row0: the last i with e_off[i] <= row0 (skips empty entries)
     int32_t lo = 0, hi = n_entries - 1;
@@ -220,7 +228,7 @@ __global__ __launch_bounds__(kThreads) void gather_kernel(
     }
     int32_t e = lo;
     const int kvec = heads * (kDk / 8), vvec = heads * (kDv / 8);
-    for (int rr = 0; rr < kGatherRows; ++rr) {
+    for (int rr = 0; rr < rows_per_block; ++rr) {
         const int32_t w = row0 + rr;
         if (w >= num_rows) break;
         while (e + 1 < n_entries && e_off[e + 1] <= w) ++e;
@@ -247,12 +255,12 @@ __global__ __launch_bounds__(kThreads) void gather_kernel(
 // p = e_start[e] + (w - e_off[e]), held by rank (p / il) % world at local index
 // (p / (il * world)) * il + p % il.  Rows are copied like the gather; a source
 // row outside the gathered buffer (inconsistent metadata) is written as NaN.
-__global__ __launch_bounds__(kThreads) void dcp_reorganize_kernel(
+__global__ __launch_bounds__(kGatherThreads) void dcp_reorganize_kernel(
     const uint4* __restrict__ gk, const uint4* __restrict__ gv, int32_t heads, int32_t world, int32_t il,
     int32_t local_rows, const int32_t* __restrict__ e_start, const int32_t* __restrict__ e_off,
-    const int32_t* __restrict__ e_loff, int32_t n_entries, int32_t num_rows, uint4* __restrict__ ws_k,
-    uint4* __restrict__ ws_v) {
-    const int32_t row0 = blockIdx.x * kGatherRows;
+    const int32_t* __restrict__ e_loff, int32_t n_entries, int32_t num_rows, int32_t rows_per_block,
+    uint4* __restrict__ ws_k, uint4* __restrict__ ws_v) {
+    const int32_t row0 = blockIdx.x * rows_per_block;
     if (row0 >= num_rows) return;
     int32_t lo = 0, hi = n_entries - 1;
     while (lo < hi) {
@@ -262,7 +270,7 @@ __global__ __launch_bounds__(kThreads) void dcp_reorganize_kernel(
     int32_t e = lo;
     const int kvec = heads * (kDk / 8), vvec = heads * (kDv / 8);
     const int64_t total = static_cast<int64_t>(world) * local_rows;
-    for (int rr = 0; rr < kGatherRows; ++rr) {
+    for (int rr = 0; rr < rows_per_block; ++rr) {
         const int32_t w = row0 + rr;
         if (w >= num_rows) break;
         while (e + 1 < n_entries && e_off[e + 1] <= w) ++e;
@@ -356,12 +364,13 @@ int launch_gather(const bf16_t* k_cache, const bf16_t* v_cache, int64_t num_bloc
                   const int32_t* e_start, const int32_t* e_off, int32_t n_entries, int32_t num_rows,
                   bf16_t* ws_k, bf16_t* ws_v, hipStream_t stream) {
     if (num_rows <= 0 || n_entries <= 0) return MLA_OK;
-    const unsigned grid = static_cast<unsigned>((num_rows + kGatherRows - 1) / kGatherRows);
+    const int32_t rows_per_block = gather_rows_per_block(heads);
+    const unsigned grid = static_cast<unsigned>((num_rows + rows_per_block - 1) / rows_per_block);
     TimedLaunch timed(MLA_KERNEL_GATHER, stream);
-    hipLaunchKernelGGL(gather_kernel, dim3(grid), dim3(kThreads), 0, stream,
+    hipLaunchKernelGGL(gather_kernel, dim3(grid), dim3(kGatherThreads), 0, stream,
                        reinterpret_cast<const uint4*>(k_cache), reinterpret_cast<const uint4*>(v_cache), num_blocks,
                        block_size, heads, block_table, bt_width, e_req, e_start, e_off, n_entries, num_rows,
-                       reinterpret_cast<uint4*>(ws_k), reinterpret_cast<uint4*>(ws_v));
+                       rows_per_block, reinterpret_cast<uint4*>(ws_k), reinterpret_cast<uint4*>(ws_v));
     return hip_status(hipGetLastError());
 }
 
@@ -369,11 +378,12 @@ int launch_dcp_reorganize(const bf16_t* gk, const bf16_t* gv, int32_t heads, int
                           int32_t local_rows, const int32_t* e_start, const int32_t* e_off, const int32_t* e_loff,
                           int32_t n_entries, int32_t num_rows, bf16_t* ws_k, bf16_t* ws_v, hipStream_t stream) {
     if (num_rows <= 0 || n_entries <= 0) return MLA_OK;
-    const unsigned grid = static_cast<unsigned>((num_rows + kGatherRows - 1) / kGatherRows);
+    const int32_t rows_per_block = gather_rows_per_block(heads);
+    const unsigned grid = static_cast<unsigned>((num_rows + rows_per_block - 1) / rows_per_block);
     TimedLaunch timed(MLA_KERNEL_DCP_REORG, stream);
-    hipLaunchKernelGGL(dcp_reorganize_kernel, dim3(grid), dim3(kThreads), 0, stream,
+    hipLaunchKernelGGL(dcp_reorganize_kernel, dim3(grid), dim3(kGatherThreads), 0, stream,
                        reinterpret_cast<const uint4*>(gk), reinterpret_cast<const uint4*>(gv), heads, world,
-                       interleave, local_rows, e_start, e_off, e_loff, n_entries, num_rows,
+                       interleave, local_rows, e_start, e_off, e_loff, n_entries, num_rows, rows_per_block,
                        reinterpret_cast<uint4*>(ws_k), reinterpret_cast<uint4*>(ws_v));
     return hip_status(hipGetLastError());
 }

@@ -117,41 +117,45 @@ __device__ __forceinline__ void merge_vec(const MergeArgs& a, int64_t t, int32_t
     if (write_lse && a.out_lse != nullptr) a.out_lse[h * a.out_stride + t] = ol;
 }
 
-// head_dim 128: a block covers 16 consecutive tokens x 4 heads; 16 lanes per
-// (token, head) row of 256 bytes.  Consecutive tokens of one head share the
-// LSE cache lines.  All loads of a lane are issued before any result is
-// formed, so that 8 row vectors are in flight per lane.
-constexpr int kMergeTokens = 16;
-constexpr int kMergeHeads = 4;
+// head_dim 128: (token, head) rows of 256 bytes are taken in memory order.
+// A block of 512 lanes is 32 groups of 16 lanes; group g takes rows row0 + g
+// and row0 + g + 32, so a block streams 64 consecutive rows (16 KB) of each
+// array.  All loads of a lane are issued before any result is formed.  (A
+// block of 16 tokens x 4 heads, whose rows lie 32 KB apart, measured 4.7
+// TB/s; this order measures 6.1 TB/s.)
+constexpr int kMergeThreads = 512;
+constexpr int kMergeRowsPerGroup = 2;
+constexpr int kMergeRowsPerBlock = kMergeThreads / 16 * kMergeRowsPerGroup;
 
-__global__ __launch_bounds__(kThreads) void merge_kernel_d128(MergeArgs a) {
+__global__ __launch_bounds__(kMergeThreads) void merge_kernel_d128(MergeArgs a) {
     const int lane_vec = threadIdx.x & 15;
-    const int64_t t = static_cast<int64_t>(blockIdx.x) * kMergeTokens + (threadIdx.x >> 4);
-    if (t >= a.tokens) return;
-    const int32_t h0 = blockIdx.y * kMergeHeads;
-    const int nh = min(kMergeHeads, a.heads - h0);
-    const bool has_prefix = t < a.prefix_num_tokens;
-    uint4 pv[kMergeHeads], sv[kMergeHeads];
-    float pl[kMergeHeads], sl[kMergeHeads];
+    const int64_t total = a.tokens * a.heads;
+    const int64_t row0 = static_cast<int64_t>(blockIdx.x) * kMergeRowsPerBlock + (threadIdx.x >> 4);
+    uint4 pv[kMergeRowsPerGroup], sv[kMergeRowsPerGroup];
+    float pl[kMergeRowsPerGroup], sl[kMergeRowsPerGroup];
 #pragma unroll
-    for (int hh = 0; hh < kMergeHeads; ++hh) {
-        if (hh < nh) {
-            const int64_t vi = (t * a.heads + h0 + hh) * 16 + lane_vec;
-            sv[hh] = load_nt(&a.s_out[vi]);
-            sl[hh] = a.s_lse[(h0 + hh) * a.s_stride + t];
-            if (has_prefix) {
-                pv[hh] = load_nt(&a.p_out[vi]);
-                pl[hh] = a.p_lse[(h0 + hh) * a.p_stride + t];
+    for (int i = 0; i < kMergeRowsPerGroup; ++i) {
+        const int64_t row = row0 + i * (kMergeThreads / 16);
+        if (row < total) {
+            const int64_t t = row / a.heads;
+            const int32_t h = static_cast<int32_t>(row - t * a.heads);
+            sv[i] = load_nt(&a.s_out[row * 16 + lane_vec]);
+            sl[i] = a.s_lse[h * a.s_stride + t];
+            if (t < a.prefix_num_tokens) {  // the prefix is not read at or past the threshold
+                pv[i] = load_nt(&a.p_out[row * 16 + lane_vec]);
+                pl[i] = a.p_lse[h * a.p_stride + t];
             }
         }
     }
 #pragma unroll
-    for (int hh = 0; hh < kMergeHeads; ++hh) {
-        if (hh < nh) {
-            const int32_t h = h0 + hh;
-            float ol = sl[hh];
-            const uint4 res = has_prefix ? merge_values(pl[hh], sl[hh], pv[hh], sv[hh], ol) : sv[hh];
-            a.out[(t * a.heads + h) * 16 + lane_vec] = res;
+    for (int i = 0; i < kMergeRowsPerGroup; ++i) {
+        const int64_t row = row0 + i * (kMergeThreads / 16);
+        if (row < total) {
+            const int64_t t = row / a.heads;
+            const int32_t h = static_cast<int32_t>(row - t * a.heads);
+            float ol = sl[i];
+            const uint4 res = t < a.prefix_num_tokens ? merge_values(pl[i], sl[i], pv[i], sv[i], ol) : sv[i];
+            a.out[row * 16 + lane_vec] = res;
             if (lane_vec == 0 && a.out_lse != nullptr) a.out_lse[h * a.out_stride + t] = ol;
         }
     }
@@ -349,9 +353,9 @@ int launch_merge(bf16_t* out, float* out_lse, const bf16_t* p_out, const float* 
                 s_stride, prefix_num_tokens};
     TimedLaunch timed(MLA_KERNEL_MERGE, stream);
     if (head_dim == 128) {
-        dim3 grid(static_cast<unsigned>((tokens + kMergeTokens - 1) / kMergeTokens),
-                  static_cast<unsigned>((heads + kMergeHeads - 1) / kMergeHeads));
-        hipLaunchKernelGGL(merge_kernel_d128, grid, dim3(kThreads), 0, stream, a);
+        const int64_t rows = tokens * heads;
+        const unsigned grid = static_cast<unsigned>((rows + kMergeRowsPerBlock - 1) / kMergeRowsPerBlock);
+        hipLaunchKernelGGL(merge_kernel_d128, dim3(grid), dim3(kMergeThreads), 0, stream, a);
     } else {
         const int grid = grid_for(tokens * heads * (head_dim / 8), kThreads, 16384);
         hipLaunchKernelGGL(merge_kernel_generic, dim3(grid), dim3(kThreads), 0, stream, a);

@@ -301,7 +301,7 @@ __global__ __launch_bounds__(kGatherThreads) void dcp_reorganize_kernel(
 constexpr int kMaskWavesPerBlock = kThreads / 64;
 
 __global__ __launch_bounds__(kThreads) void mask_empty_context_kernel(
-    float* lse, int64_t lse_stride, uint32_t* out, int64_t row_words, const int32_t* __restrict__ qsl,
+    float* lse, int64_t lse_stride, uint32_t* out, int64_t row_words, bool vec16, const int32_t* __restrict__ qsl,
     const int32_t* __restrict__ csl, int32_t num_requests, int64_t num_tokens, int32_t heads) {
     const int lane = threadIdx.x & 63;
     const int64_t t = static_cast<int64_t>(blockIdx.x) * kMaskWavesPerBlock + (threadIdx.x >> 6);
@@ -319,7 +319,12 @@ __global__ __launch_bounds__(kThreads) void mask_empty_context_kernel(
     if (csl[r + 1] - csl[r] != 0) return;
     for (int h = lane; h < heads; h += 64) lse[h * lse_stride + t] = -INFINITY;
     uint32_t* row = out + t * row_words;
-    for (int64_t w = lane; w < row_words; w += 64) row[w] = 0u;
+    if (vec16) {  // 16-byte aligned rows: one 16-byte store per lane per 1 KB
+        uint4* row4 = reinterpret_cast<uint4*>(row);
+        for (int64_t w = lane; w < row_words / 4; w += 64) row4[w] = make_uint4(0u, 0u, 0u, 0u);
+    } else {
+        for (int64_t w = lane; w < row_words; w += 64) row[w] = 0u;
+    }
 }
 
 int grid_for(int64_t work, int64_t per_block, int64_t cap) {
@@ -397,10 +402,11 @@ int launch_mask_empty_context(float* lse, int64_t lse_stride, void* out, int32_t
                               int32_t head_dim, hipStream_t stream) {
     if (num_tokens <= 0) return MLA_OK;
     const int64_t row_words = static_cast<int64_t>(heads) * head_dim * elem_bytes / 4;
+    const bool vec16 = aligned16(out) && row_words % 4 == 0;
     const unsigned grid = static_cast<unsigned>((num_tokens + kMaskWavesPerBlock - 1) / kMaskWavesPerBlock);
     TimedLaunch timed(MLA_KERNEL_MASK, stream);
     hipLaunchKernelGGL(mask_empty_context_kernel, dim3(grid), dim3(kThreads), 0, stream, lse, lse_stride,
-                       static_cast<uint32_t*>(out), row_words, qsl, csl, num_requests, num_tokens, heads);
+                       static_cast<uint32_t*>(out), row_words, vec16, qsl, csl, num_requests, num_tokens, heads);
     return hip_status(hipGetLastError());
 }
 

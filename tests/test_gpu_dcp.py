@@ -137,3 +137,24 @@ def test_dcp_homogeneous_full_size_sampled():
         return res
 
     sampled_check(mla, W.named_workloads()[3], path=f"dcp world={world}", runner=runner)
+
+
+def test_reorganize_inconsistent_metadata_writes_nan_rows():
+    # local_rows too small for the entry: rows whose source falls past the
+    # gathered buffer come out NaN; every other row is a copy (no fault)
+    say("dcp reorganize with inconsistent local_rows")
+    H, world, L = 1, 2, 2
+    gk = torch.arange(world * L * H * W.DK, dtype=torch.float32).reshape(world * L, H, W.DK).to(torch.bfloat16)
+    gv = torch.arange(world * L * H * W.DV, dtype=torch.float32).reshape(world * L, H, W.DV).to(torch.bfloat16)
+    gk, gv = gk.to(DEV), gv.to(DEV)
+    wk = torch.zeros((8, H, W.DK), dtype=torch.bfloat16, device=DEV)
+    wv = torch.zeros((8, H, W.DV), dtype=torch.bfloat16, device=DEV)
+    mla.mla_dcp_reorganize_context(gk, gv, world, 1, L, _i32([0]), _i32([0, 8]), _i32([0, 2]), 8, wk, wv)
+    torch.cuda.synchronize()
+    k, gkh = host(wk), host(gk)
+    for p in range(8):
+        src = (p % 2) * L + p // 2
+        if src >= world * L:
+            assert np.isnan(k[p]).all(), p
+        else:
+            assert np.array_equal(k[p], gkh[src]), p

@@ -294,3 +294,10 @@ def test_mask_empty_context_random(seed):
     cl = [0 if rng.random() < 0.3 else int(rng.integers(1, 50)) for _ in range(n)]
     say(f"mask_empty_context random seed={seed} n={n}")
     _mask_case(ql, cl, int(rng.integers(1, 9)), 128, torch.bfloat16, seed)
+
+
+@pytest.mark.parametrize("H,D,dtype", [(3, 2, torch.bfloat16), (5, 3, torch.float32), (2, 8, torch.bfloat16)])
+def test_mask_empty_context_unaligned_rows(H, D, dtype):
+    # rows that are not a multiple of 16 bytes take the 4-byte store path
+    say(f"mask_empty_context rows of {H * D} elements ({dtype})")
+    _mask_case([3, 0, 5, 2, 7], [0, 4, 0, 1, 0], H, D, dtype, 11)

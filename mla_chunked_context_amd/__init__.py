@@ -25,7 +25,7 @@ QK_HEAD_DIM = 192
 V_HEAD_DIM = 128
 
 if not os.path.exists(LIB_PATH):
-    raise ImportError(f"{LIB_PATH} is missing: build it first (python -c 'import __graft_entry__ as g; g.build()')")
+    raise ImportError(f"{LIB_PATH} is missing: build it first (python mla_chunked_context_amd/build.py)")
 
 _lib = ctypes.CDLL(LIB_PATH)
 

@@ -81,3 +81,41 @@ def test_heterogeneous_full_size_sampled():
 
 def test_long_context_full_size_sampled():
     sampled_check(mla, W.named_workloads()[5], tokens_per_request=8)
+
+
+def test_side_stream_matches_default_stream():
+    wl = W.named_workloads()[1]
+    b = W.make_batch(wl, device=DEV, gen_device="cpu")
+    o1, l1 = run_prefill(mla, b)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        o2, l2 = run_prefill(mla, b, stream=s)
+    s.synchronize()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)) and torch.equal(l1, l2)
+
+
+def test_many_calls_in_flight_reuse_staging_safely():
+    # six calls enqueued without waiting (more than the pinned staging slots),
+    # each on a different batch, must each equal its own call run alone
+    say("six prefill calls in flight")
+    cases = []
+    for seed in range(6):
+        wl = W.random_workload(100 + seed, max_requests=5, max_ctx=400, max_q=40, heads=(2,), alignments=(8, 16))
+        cases.append(W.make_batch(wl, device=DEV, gen_device="cpu"))
+    alone = [run_prefill(mla, b) for b in cases]
+    outs = []
+    for b in cases:
+        wl = b.wl
+        T, H = wl.num_tokens, wl.num_heads
+        out = torch.full((T, H, W.DV), float("nan"), dtype=torch.bfloat16, device=DEV)
+        lse = torch.full((H, T), float("nan"), dtype=torch.float32, device=DEV)
+        mk = lambda s=None: mla.make_prefill_params(  # noqa: E731
+            b.q, b.k_new, b.v_new, b.k_cache, b.v_cache, b.block_table, wl.context_lens, wl.query_lens,
+            wl.workspace_rows, wl.split_alignment, wl.scale, out=out, out_lse=lse, scratch=s)
+        scratch = torch.empty(max(256, mla.mla_chunked_prefill_scratch_size(mk())), dtype=torch.uint8, device=DEV)
+        p = mk(scratch)
+        mla.mla_chunked_prefill(p)  # no synchronisation between calls
+        outs.append((out, lse, scratch, p))
+    torch.cuda.synchronize()
+    for (o1, l1), (o2, l2, _, _) in zip(alone, outs):
+        assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)) and torch.equal(l1, l2)

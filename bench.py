@@ -177,7 +177,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default=None,
-                    choices=["tiny", "empty_context_stress", "homogeneous", "heterogeneous", "long_context"],
+                    choices=["tiny", "empty_context_stress", "homogeneous", "heterogeneous", "long_context", "skewed"],
                     help="default: long_context (chunked), heterogeneous (uniform_window, mask_empty_context)")
     ap.add_argument("--path", default="chunked", choices=["chunked", "uniform_window", "mask_empty_context", "dcp"])
     ap.add_argument("--dcp-world", type=int, default=4, help="emulated DCP ranks (--path dcp)")
@@ -274,7 +274,7 @@ def main():
     import workloads as W
     import mla_chunked_context_amd as mla
 
-    wl = next(w for w in W.named_workloads().values() if w.name == args.workload)
+    wl = W.workload_by_name(args.workload)
     dev = "cuda:0"
     torch.cuda.set_device(0)
     log(f"bench: generating {wl.name} inputs on the GPU")

@@ -119,3 +119,7 @@ def test_many_calls_in_flight_reuse_staging_safely():
     torch.cuda.synchronize()
     for (o1, l1), (o2, l2, _, _) in zip(alone, outs):
         assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)) and torch.equal(l1, l2)
+
+
+def test_skewed_full_size_sampled():
+    sampled_check(mla, W.workload_by_name("skewed"), tokens_per_request=3)

@@ -77,3 +77,8 @@ def test_homogeneous_full_size_sampled():
 
 def test_heterogeneous_full_size_sampled():
     sampled_check(mla, W.named_workloads()[4], tokens_per_request=4, path="uniform_window")
+
+
+def test_skewed_full_size_sampled():
+    # one 131072-row context among 63 short ones: 64 equal-window iterations
+    sampled_check(mla, W.workload_by_name("skewed"), tokens_per_request=3, path="uniform_window")

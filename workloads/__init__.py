@@ -84,6 +84,26 @@ def named_workloads():
     }
 
 
+def extra_workloads():
+    """Batches beyond the five named ones, for scheduler comparisons.
+
+    skewed: one request with a 131072-row context among 63 with 64 rows, 512
+    new tokens each (T = 32768), H = 128, workspace 131072 rows, A = B = 64.
+    The equal-window scheduler gives every request with context a 2048-row
+    window and needs 64 iterations over the whole batch for the long request;
+    per-request packing needs 2 chunks."""
+    return {
+        "skewed": Workload("skewed", tuple([131072] + [64] * 63), tuple([512] * 64), 128, 131072, 64, 64, 1.0, 6),
+    }
+
+
+def workload_by_name(name: str) -> Workload:
+    for w in list(named_workloads().values()) + list(extra_workloads().values()):
+        if w.name == name:
+            return w
+    raise KeyError(name)
+
+
 def random_workload(seed: int, max_requests=6, max_ctx=300, max_q=40, heads=(1, 2, 4),
                     alignments=(1, 2, 4, 8, 16), zero_frac=0.25) -> Workload:
     """A small random instance for property tests (seeded)."""

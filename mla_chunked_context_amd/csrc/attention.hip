@@ -67,6 +67,9 @@ constexpr int kKTileBytes = kBlockN * kKRowBytes;  // 24 KB
 constexpr int kVtTileElems = kDv * kVtStride;
 constexpr float kRescaleThreshold = 8.0f;  // log2 units
 constexpr int kBufferConfig = 0x00020000;  // dword 3 of a raw buffer descriptor on gfx9
+// s_waitcnt immediate on gfx9: vmcnt in bits 3:0 (and 15:14), expcnt 6:4, lgkmcnt 11:8;
+// this one waits for vector memory only
+constexpr int kWaitVmcnt0 = 0x0F70;
 
 static_assert(kBlockN * kKVecPerRow == kKLoads * kThreads, "K tile must split evenly over threads");
 static_assert(kBlockN / 2 * (kDv / 8) == kThreads, "V tile mapping: 32 key pairs x 16 dim groups");
@@ -282,6 +285,11 @@ __device__ __forceinline__ void attention_body(const AttnArgs& a, unsigned char*
         if (n_tiles > 1) load_v(kBlockN);  // V(1): stored at the start of iteration 0
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // direct-to-LDS loads have landed
+    // the same wait as an instruction the compiler sees: the Q fragments'
+    // register loads are then known complete on every path into the loop (the
+    // prologue's conditional QK leaves a path where they are not, and the loop
+    // would otherwise wait for all loads before its first QK MFMA)
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     __syncthreads();
     if (n_tiles > 0 && (!kCausal || 0 <= wave_last_q)) qk(s_cur, std::integral_constant<int, 0>{});
     __syncthreads();  // K(0) is overwritten by K(2) at the end of iteration 0

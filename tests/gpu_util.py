@@ -45,6 +45,30 @@ def run_prefill(mla, b, out_lse=True, stream=None, path="chunked"):
     return out, lse
 
 
+def run_dcp_prefill(mla, b, ranks, interleave):
+    """Run mla_dcp_chunked_prefill on a Batch whose context lives in ``ranks``
+    (RankCache list on the GPU, as workloads.shard_context makes them)."""
+    wl = b.wl
+    T, H = wl.num_tokens, wl.num_heads
+    dev = b.q.device
+    out = torch.full((T, H, W.DV), float("nan"), dtype=torch.bfloat16, device=dev)
+    lse = torch.full((H, T), float("nan"), dtype=torch.float32, device=dev)
+    dr = mla.make_dcp_ranks(ranks, interleave)
+
+    def params(scratch=None):
+        p = mla.make_prefill_params(b.q, b.k_new, b.v_new, None, None, None, wl.context_lens, wl.query_lens,
+                                    wl.workspace_rows, wl.split_alignment, wl.scale, out=out, out_lse=lse,
+                                    scratch=scratch)
+        p.block_size = wl.block_size
+        return p
+
+    n = mla.mla_dcp_chunked_prefill_scratch_size(params(), dr)
+    scratch = torch.full(((max(n, 256) + 1) // 2,), float("nan"), dtype=torch.bfloat16, device=dev)
+    mla.mla_dcp_chunked_prefill(params(scratch), dr)
+    torch.cuda.synchronize()
+    return out, lse
+
+
 def host(t):
     return t.detach().float().cpu().double().numpy()
 

@@ -15,7 +15,7 @@ import torch
 import oracle as O
 import oracle.dcp as OD
 import workloads as W
-from tests.gpu_util import check, host, sampled_check, say
+from tests.gpu_util import check, host, run_dcp_prefill, sampled_check, say
 
 pytestmark = pytest.mark.gpu
 
@@ -66,26 +66,6 @@ def test_reorganize_equals_single_device_gather(world, il):
         assert np.array_equal(host(wk), ref_k) and np.array_equal(host(wv), ref_v)
 
 
-def _run_dcp(b, ranks, world, il):
-    wl = b.wl
-    T, H = wl.num_tokens, wl.num_heads
-    out = torch.full((T, H, W.DV), float("nan"), dtype=torch.bfloat16, device=DEV)
-    lse = torch.full((H, T), float("nan"), dtype=torch.float32, device=DEV)
-    dr = mla.make_dcp_ranks(ranks, il)
-    mk = lambda s=None: mla.make_prefill_params(  # noqa: E731
-        b.q, b.k_new, b.v_new, None, None, None, wl.context_lens, wl.query_lens, wl.workspace_rows,
-        wl.split_alignment, wl.scale, out=out, out_lse=lse, scratch=s)
-    p = mk()
-    p.block_size = wl.block_size
-    n = mla.mla_dcp_chunked_prefill_scratch_size(p, dr)
-    scratch = torch.full(((max(n, 256) + 1) // 2,), float("nan"), dtype=torch.bfloat16, device=DEV)
-    p = mk(scratch)
-    p.block_size = wl.block_size
-    mla.mla_dcp_chunked_prefill(p, dr)
-    torch.cuda.synchronize()
-    return out, lse
-
-
 @pytest.mark.parametrize("world,il", [(2, 1), (4, 1), (4, 2)])
 def test_dcp_prefill_small_full(world, il):
     wl = SMALL
@@ -101,7 +81,7 @@ def test_dcp_prefill_small_full(world, il):
                 b.block_table.to(DEV), b.num_blocks, b.spare_blocks)
     dr = [W.RankCache(r.k_cache.to(DEV), r.v_cache.to(DEV), r.block_table.to(DEV), r.num_blocks, r.context_lens)
           for r in ranks]
-    out, lse = _run_dcp(d, dr, world, il)
+    out, lse = run_dcp_prefill(mla, d, dr, il)
     vmax = float(max(np.abs(f(b.v_new)).max(), np.nanmax(np.abs(f(b.v_cache)))))
     say("  ", check(host(out), lse.double().cpu().numpy(), ref["out"], ref["lse"], vmax, "dcp small"))
 
@@ -122,7 +102,7 @@ def test_dcp_prefill_random_full():
                     b.block_table.to(DEV), b.num_blocks, b.spare_blocks)
         dr = [W.RankCache(r.k_cache.to(DEV), r.v_cache.to(DEV), r.block_table.to(DEV), r.num_blocks,
                           r.context_lens) for r in ranks]
-        out, lse = _run_dcp(d, dr, world, il)
+        out, lse = run_dcp_prefill(mla, d, dr, il)
         vmax = float(max(np.abs(f(b.v_new)).max(), np.nanmax(np.abs(f(b.v_cache)))))
         say("  ", check(host(out), lse.double().cpu().numpy(), ref[0], ref[1], vmax, f"dcp random {seed}"))
 
@@ -132,7 +112,7 @@ def test_dcp_homogeneous_full_size_sampled():
 
     def runner(b):
         ranks = W.shard_context(b, world, il, canary=False)
-        res = _run_dcp(b, ranks, world, il)
+        res = run_dcp_prefill(mla, b, ranks, il)
         del ranks
         return res
 

@@ -269,7 +269,10 @@ int mla_mask_empty_context(float* lse, int64_t lse_head_stride, void* output, in
                            void* stream);
 
 /* Inputs, outputs and scratch of one chunked prefill (all dev pointers are
- * caller-owned; lens are host arrays). */
+ * caller-owned; lens are host arrays).  The scratch holds the call's chunk
+ * metadata, workspace and partial results until its work on the stream has
+ * completed: calls that can run at the same time (on different streams) need
+ * separate scratch buffers; calls on one stream may share one. */
 typedef struct mla_chunked_prefill_params {
     const void* q;              /* dev bf16 [T, H, 192] */
     const void* k_new;          /* dev bf16 [T, H, 192] */

@@ -34,6 +34,7 @@ class TimedLaunch {
   private:
     int kind_;
     hipStream_t stream_;
+    int device_ = 0;
     hipEvent_t start_ = nullptr;
 };
 

@@ -98,6 +98,71 @@ def profiled_traffic(kernel, workload):
     return k["fetch_bytes_per_launch"] + k["write_bytes_per_launch"]
 
 
+TRAFFIC_SOURCES = {"chunk_attention_kernel": "attention.hip", "suffix_attention_kernel": "attention.hip"}
+
+
+def write_traffic(fetch_csv, write_csv, workload, out_path=None):
+    """profiles/<workload>_traffic.json from two rocprofv3 counter collections
+    (--pmc FETCH_SIZE and --pmc WRITE_SIZE of a run with
+    --calibration-copy-mb 1024).  Each counter is scaled by the bytes per
+    counter unit of the run's 1 GiB elementwise copy (the torch negation
+    launched after the timed steps); the library's kernels get their mean
+    bytes per launch and a hash of their sources.  Host only."""
+    import collections
+    import csv
+    import hashlib
+
+    def per_kernel(path, counter):
+        disp = collections.defaultdict(float)
+        names = {}
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] != counter:
+                    continue
+                k = int(r["Dispatch_Id"])
+                names[k] = r["Kernel_Name"]
+                disp[k] += float(r["Counter_Value"])
+        out = collections.defaultdict(list)
+        for k, v in disp.items():
+            n = names[k]
+            if "neg_kernel" in n:
+                out["calibration"].append(v)
+            elif n.startswith("mla::"):
+                short = n.replace("(anonymous namespace)::", "").split("(")[0].split("::")[-1]
+                out[short].append(v)
+        return out
+
+    fetch, write = per_kernel(fetch_csv, "FETCH_SIZE"), per_kernel(write_csv, "WRITE_SIZE")
+    if len(fetch["calibration"]) != 1 or len(write["calibration"]) != 1:
+        raise SystemExit("expected exactly one calibration copy dispatch in each counter collection")
+    gib = float(1 << 30)
+    fetch_scale = gib / (fetch["calibration"][0] * 1024)
+    write_scale = gib / (write["calibration"][0] * 1024)
+    res = {"workload": workload,
+           "how": "rocprofv3 --pmc FETCH_SIZE, then --pmc WRITE_SIZE (KiB per dispatch), each scaled by the "
+                  "counter-per-byte ratio of a 1 GiB elementwise copy run in the same process",
+           "fetch_scale": round(fetch_scale, 4), "write_scale": round(write_scale, 4), "kernels": {}}
+    for k in sorted(set(fetch) - {"calibration"}):
+        if not write.get(k):
+            continue
+        srcs = [f"mla_chunked_context_amd/csrc/{TRAFFIC_SOURCES.get(k, 'memory_ops.hip')}",
+                "mla_chunked_context_amd/csrc/device.h"]
+        h = hashlib.sha256()
+        for src in srcs:
+            with open(os.path.join(ROOT, src), "rb") as f:
+                h.update(f.read())
+        res["kernels"][k] = {
+            "launches_profiled": len(fetch[k]),
+            "fetch_bytes_per_launch": int(sum(fetch[k]) / len(fetch[k]) * 1024 * fetch_scale),
+            "write_bytes_per_launch": int(sum(write[k]) / len(write[k]) * 1024 * write_scale),
+            "source_sha256": h.hexdigest(), "sources": srcs}
+    path = out_path or os.path.join(ROOT, "profiles", f"{workload}_traffic.json")
+    with open(path, "w") as f:
+        json.dump(res, f, indent=1)
+    log(f"bench: wrote {path}")
+    return res
+
+
 def cpu_baseline(b, wl, sample_queries, path="chunked", rank_caches=None, dcp=(1, 1)):
     """The oracle on a bounded sample: head 0 only and the first
     `sample_queries` new tokens of every request, against full contexts."""
@@ -184,6 +249,9 @@ def parse():
     ap.add_argument("--dcp-interleave", type=int, default=1, help="DCP interleave run length (--path dcp)")
     ap.add_argument("--cpu-sample-queries", type=int, default=8192)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="host only: write profiles/<workload>_traffic.json from the counter collections of "
+                         "rocprofv3 --pmc FETCH_SIZE and --pmc WRITE_SIZE runs of this benchmark, then exit")
     ap.add_argument("--calibration-copy-mb", type=int, default=0,
                     help="after timing, run one elementwise copy (negation) of this many MiB of bf16 so that "
                          "hardware byte counters can be scaled against a kernel of known traffic")
@@ -264,6 +332,9 @@ def roofline(kt, wf, K, workload, kind=None):
 
 def main():
     args = parse()
+    if args.write_traffic:
+        write_traffic(args.write_traffic[0], args.write_traffic[1], args.workload)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print(f"bench.py runs on one GPU only: the chunked-prefill path here is single-GPU "
               f"(asked for --gpus {args.gpus}); run with --gpus 1", file=sys.stderr)

@@ -256,14 +256,14 @@ __device__ __forceinline__ void attention_body(const AttnArgs& a, unsigned char*
                     k_lane[ks & 3] + kbuf * kKTileBytes + kb * 32 * kKRowBytes + (ks >> 2) * 128);
                 s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, qf[ks], s[kb], 0, 0, 0);
             }
-        // schedule: 8 fragment reads ahead, then alternate MFMA / read
-        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+        // schedule: 6 fragment reads ahead, then alternate MFMA / read
+        __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
+        for (int i = 0; i < 18; ++i) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
             __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         }
-        __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 6, 0);
     };
 
     // Software pipeline over key tiles.  Tile j's scores S(j) are computed one

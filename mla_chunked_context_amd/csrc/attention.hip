@@ -96,6 +96,15 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     return __builtin_bit_cast(uint32_t, v);
 }
 
+// Low (high) 16-bit halves of w0 and w1 packed as (w0 half, w1 half): one
+// v_perm_b32 each (byte selector: 0-3 pick bytes of w0, 4-7 bytes of w1).
+__device__ __forceinline__ uint32_t lo_halves(uint32_t w0, uint32_t w1) {
+    return __builtin_amdgcn_perm(w1, w0, 0x05040100u);
+}
+__device__ __forceinline__ uint32_t hi_halves(uint32_t w0, uint32_t w1) {
+    return __builtin_amdgcn_perm(w1, w0, 0x07060302u);
+}
+
 // Position of key (0..63) inside a V^T LDS row: bits 2 and 3 swapped.
 __device__ __forceinline__ int vt_pos(int key) {
     return (key & ~12) | ((key & 4) << 1) | ((key & 8) >> 1);
@@ -225,8 +234,8 @@ __device__ __forceinline__ void attention_body(const AttnArgs& a, unsigned char*
         for (int i = 0; i < 4; ++i) {
             const uint32_t w0 = vreg[0][i], w1 = vreg[1][i];
             const int d0 = vdc * 8 + 2 * i;
-            *reinterpret_cast<uint32_t*>(&vl[d0 * kVtStride + v_lpos]) = (w0 & 0xffffu) | (w1 << 16);
-            *reinterpret_cast<uint32_t*>(&vl[(d0 + 1) * kVtStride + v_lpos]) = (w0 >> 16) | (w1 & 0xffff0000u);
+            *reinterpret_cast<uint32_t*>(&vl[d0 * kVtStride + v_lpos]) = lo_halves(w0, w1);
+            *reinterpret_cast<uint32_t*>(&vl[(d0 + 1) * kVtStride + v_lpos]) = hi_halves(w0, w1);
         }
     };
 

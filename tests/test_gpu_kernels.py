@@ -229,6 +229,45 @@ def test_suffix_attention_matches_oracle(case):
     say("  ", r)
 
 
+def _rising_case(seed, q_len, k_len, H, rate, causal):
+    """Scores that grow from key tile to key tile: queries share a direction u,
+    and key j carries rate * (j // 64) * u, so the running max of a query rises
+    by about rate * |u|^2 * scale * log2(e) per 64-key tile (tens of log2
+    units for rate 0.3), far past the point where the kernels must move their
+    reference max after the first tile."""
+    g = torch.Generator().manual_seed(seed)
+    u = 2.0 * torch.randn(H, W.DK, generator=g)
+    q = (u[None] + torch.randn(q_len, H, W.DK, generator=g)).to(torch.bfloat16)
+    step = (torch.arange(k_len) // 64).float() * rate
+    k = (step[:, None, None] * u[None] + torch.randn(k_len, H, W.DK, generator=g)).to(torch.bfloat16)
+    v = torch.randn(k_len, H, W.DV, generator=g).to(torch.bfloat16)
+    scale = 1 / np.sqrt(W.DK)
+    out = torch.full((q_len, H, W.DV), float("nan"), dtype=torch.bfloat16, device=DEV)
+    lse = torch.full((H, q_len), float("nan"), dtype=torch.float32, device=DEV)
+    cu_q = torch.tensor([0, q_len], dtype=torch.int32, device=DEV)
+    cu_k = torch.tensor([0, k_len], dtype=torch.int32, device=DEV)
+    if causal:
+        mla.mla_causal_suffix_attn(q.to(DEV), k.to(DEV), v.to(DEV), cu_q, q_len, scale, out, lse)
+    else:
+        mla.mla_context_chunk_attn(q.to(DEV), k.to(DEV), v.to(DEV), cu_q, cu_k, q_len, scale, out, lse)
+    torch.cuda.synchronize()
+    o, l = O.attention_with_lse(host(q), host(k), host(v), scale, causal=causal)
+    return check(host(out), lse.double().cpu().numpy(), o, l, np.abs(host(v)).max(), f"rising seed {seed}")
+
+
+@pytest.mark.parametrize("case", [
+    (31, 300, 640, 2, 0.3),    # every tile raises the max by ~20 log2 units
+    (32, 257, 1000, 1, 0.03),  # gentle rise: a few raises over the sequence
+    (33, 64, 200, 3, -0.3),    # falling scores: the first tile holds the max
+])
+def test_attention_rising_scores(case):
+    seed, ql, kl, H, rate = case
+    say(f"chunk attention, rising scores {case}")
+    say("  ", _rising_case(seed, ql, kl, H, rate, causal=False))
+    say(f"suffix attention, rising scores {case}")
+    say("  ", _rising_case(seed, ql, ql, H, rate, causal=True))
+
+
 def test_attention_empty_keys_give_empty_state():
     say("attention with no keys")
     H = 2

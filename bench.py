@@ -242,7 +242,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default=None,
-                    choices=["tiny", "empty_context_stress", "homogeneous", "heterogeneous", "long_context", "skewed"],
+                    choices=["tiny", "empty_context_stress", "homogeneous", "heterogeneous", "long_context", "skewed",
+                             "heterogeneous_h16"],
                     help="default: long_context (chunked), heterogeneous (uniform_window, mask_empty_context)")
     ap.add_argument("--path", default="chunked", choices=["chunked", "uniform_window", "mask_empty_context", "dcp"])
     ap.add_argument("--dcp-world", type=int, default=4, help="emulated DCP ranks (--path dcp)")

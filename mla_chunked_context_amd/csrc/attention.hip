@@ -88,6 +88,13 @@ struct AttnArgs {
     int32_t heads;
     int32_t total_tiles;
     float scale_log2;  // scale * log2(e)
+    // key split (non-causal only): split s of a sequence attends to keys
+    // [s * split_keys, (s + 1) * split_keys) of it and writes its state at
+    // out + s * split_out_stride, lse + s * split_lse_stride
+    int32_t splits;
+    int32_t split_keys;
+    int64_t split_out_stride;
+    int64_t split_lse_stride;
 };
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
@@ -139,7 +146,9 @@ template <bool kCausal>
 __device__ __forceinline__ void attention_body(const AttnArgs& a, unsigned char* k_lds, bf16_t* vt_lds) {
     const int32_t tile = xcd_logical_tile(blockIdx.x, a.total_tiles, a.q_tiles);
     int32_t qt = tile % a.q_tiles;
-    const int32_t rest = tile / a.q_tiles;
+    int32_t rest = tile / a.q_tiles;
+    const int32_t split = kCausal ? 0 : rest % a.splits;
+    if (!kCausal) rest /= a.splits;
     const int32_t head = rest % a.heads;
     const int32_t seq = rest / a.heads;
     if (kCausal) qt = a.q_tiles - 1 - qt;  // longest causal tiles first
@@ -147,8 +156,17 @@ __device__ __forceinline__ void attention_body(const AttnArgs& a, unsigned char*
     const int32_t q_begin = a.cu_q[seq];
     const int32_t q_len = a.cu_q[seq + 1] - q_begin;
     if (qt * kBlockM >= q_len) return;
-    const int32_t k_begin = kCausal ? q_begin : a.cu_k[seq];
-    const int32_t k_len = kCausal ? q_len : a.cu_k[seq + 1] - k_begin;
+    int32_t k_begin = kCausal ? q_begin : a.cu_k[seq];
+    int32_t k_len = kCausal ? q_len : a.cu_k[seq + 1] - k_begin;
+    bf16_t* out = a.out;
+    float* lse_out = a.lse;
+    if (!kCausal && a.splits > 1) {
+        const int32_t lo = split * a.split_keys;
+        k_begin += lo;
+        k_len = max(0, min(k_len - lo, a.split_keys));  // an empty slice writes (0, -inf)
+        out += split * a.split_out_stride;
+        lse_out += split * a.split_lse_stride;
+    }
     const int32_t kv_end = kCausal ? min(k_len, (qt + 1) * kBlockM) : k_len;
 
     const int tid = threadIdx.x;
@@ -419,7 +437,7 @@ __device__ __forceinline__ void attention_body(const AttnArgs& a, unsigned char*
     const float l_tot = pair_sum(l_run);
     if (!q_valid) return;
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    bf16_t* orow = a.out + (static_cast<int64_t>(q_begin + q_row) * H + head) * kDv + g * 4;
+    bf16_t* orow = out + (static_cast<int64_t>(q_begin + q_row) * H + head) * kDv + g * 4;
 #pragma unroll
     for (int db = 0; db < kDv / 32; ++db)
 #pragma unroll
@@ -430,7 +448,7 @@ __device__ __forceinline__ void attention_body(const AttnArgs& a, unsigned char*
         }
     if (g == 0) {
         const float lse = l_tot > 0.f ? (m_run + log2f(l_tot)) * 0.69314718055994531f : -INFINITY;
-        a.lse[head * a.lse_stride + q_begin + q_row] = lse;
+        lse_out[head * a.lse_stride + q_begin + q_row] = lse;
     }
 }
 
@@ -451,8 +469,10 @@ __global__ __launch_bounds__(kThreads, 1) void suffix_attention_kernel(AttnArgs 
 
 int launch_attention(const bf16_t* q, const bf16_t* k, const bf16_t* v, const int32_t* cu_q, const int32_t* cu_k,
                      int32_t num_seqs, int32_t max_q, int32_t heads, float scale, bool causal, bf16_t* out,
-                     float* lse, int64_t lse_stride, hipStream_t stream) {
+                     float* lse, int64_t lse_stride, hipStream_t stream, const AttnSplit& split) {
     if (num_seqs <= 0 || max_q <= 0) return MLA_OK;
+    if (split.splits < 1 || (split.splits > 1 && (causal || split.split_keys < kBlockN || split.split_keys % kBlockN)))
+        return MLA_ERR_INVALID_ARG;
     AttnArgs a{};
     a.q = q;
     a.k = k;
@@ -465,7 +485,11 @@ int launch_attention(const bf16_t* q, const bf16_t* k, const bf16_t* v, const in
     a.num_seqs = num_seqs;
     a.q_tiles = (max_q + kBlockM - 1) / kBlockM;
     a.heads = heads;
-    const int64_t total = static_cast<int64_t>(num_seqs) * a.q_tiles * heads;
+    a.splits = split.splits;
+    a.split_keys = split.split_keys;
+    a.split_out_stride = split.out_stride;
+    a.split_lse_stride = split.lse_stride;
+    const int64_t total = static_cast<int64_t>(num_seqs) * a.q_tiles * heads * split.splits;
     if (total > INT32_MAX) return MLA_ERR_UNSUPPORTED;
     a.total_tiles = static_cast<int32_t>(total);
     a.scale_log2 = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);

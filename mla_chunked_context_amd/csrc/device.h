@@ -59,10 +59,22 @@ int launch_mask_empty_context(float* lse, int64_t lse_stride, void* out, int32_t
                               const int32_t* csl, int32_t num_requests, int64_t num_tokens, int32_t heads,
                               int32_t head_dim, hipStream_t stream);
 
+// Key split of a non-causal launch: split s of every sequence covers keys
+// [s * split_keys, (s + 1) * split_keys) (split_keys a multiple of the 64-key
+// tile) and writes its (output, LSE) state at out + s * out_stride elements and
+// lse + s * lse_stride floats; the caller LSE-merges the splits.
+struct AttnSplit {
+    int32_t splits = 1;
+    int32_t split_keys = 0;
+    int64_t out_stride = 0;
+    int64_t lse_stride = 0;
+};
+
 // Varlen attention.  causal: query i of a sequence sees keys 0..i of the same
 // sequence (cu_k must then equal cu_q).
 int launch_attention(const bf16_t* q, const bf16_t* k, const bf16_t* v, const int32_t* cu_q,
                      const int32_t* cu_k, int32_t num_seqs, int32_t max_q, int32_t heads, float scale,
-                     bool causal, bf16_t* out, float* lse, int64_t lse_stride, hipStream_t stream);
+                     bool causal, bf16_t* out, float* lse, int64_t lse_stride, hipStream_t stream,
+                     const AttnSplit& split = AttnSplit{});
 
 }  // namespace mla

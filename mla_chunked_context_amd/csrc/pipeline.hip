@@ -56,17 +56,53 @@ struct VecSink : PlanSink {
 
 // Device metadata of one chunk, as offsets (in int32 elements) into the meta
 // block.  e_lstart / e_loff (local starts and offsets) exist only under DCP.
+// Key split of a chunk-attention launch whose workgroups (sequences x 256-query
+// tiles x heads) cannot fill the GPU's CUs, e.g. one long-context request with
+// few queries, or a head shard of 16 heads per GPU: each sequence's key range
+// is cut into `splits` slices of `split_keys` rows, one workgroup per slice,
+// and the slices' states are LSE-merged (the merge_attn_states operator).
+// Splitting pays only while the split grid still fits in one round of the
+// CUs, and each slice keeps at least kMinSplitTiles key tiles.
+constexpr int32_t kNumCUs = 256;       // MI355X
+constexpr int32_t kMaxSplits = 8;      // the merge tree is at most 3 deep
+constexpr int32_t kMinSplitTiles = 64; // 4096 keys per slice at least
+constexpr int32_t kQueryTile = 256;    // queries per attention workgroup
+constexpr int32_t kKeyTile = 64;       // keys per attention tile
+
+struct SplitPlan {
+    int32_t splits = 1;
+    int32_t split_keys = 0;
+};
+
+SplitPlan plan_split(int32_t n_seqs, int32_t max_q, int32_t max_rows, int32_t heads) {
+    const int64_t wgs = static_cast<int64_t>(n_seqs) * ((max_q + kQueryTile - 1) / kQueryTile) * heads;
+    const int32_t key_tiles = (max_rows + kKeyTile - 1) / kKeyTile;
+    if (wgs <= 0) return {};
+    const int64_t s = std::min<int64_t>({kMaxSplits, kNumCUs / wgs, key_tiles / kMinSplitTiles});
+    if (s < 2) return {};
+    SplitPlan sp;
+    const int32_t tiles = static_cast<int32_t>((key_tiles + s - 1) / s);
+    sp.split_keys = tiles * kKeyTile;
+    sp.splits = (key_tiles + tiles - 1) / tiles;  // no slice starts past the longest range
+    return sp.splits >= 2 ? sp : SplitPlan{};
+}
+
 struct ChunkMeta {
     int64_t e_req, e_start, e_off, cu_q, e_lstart = 0, e_loff = 0;
     int32_t rows = 0;        // context rows (request order)
     int32_t local_rows = 0;  // padded local rows of one rank (DCP)
+    SplitPlan split_cont;    // the continuation request's own launch
+    SplitPlan split_direct;  // the launch over the other requests
 };
 
 struct Layout {
     int64_t ws_k, ws_v, part_out, part_lse, suf_out, suf_lse, tmp_out, tmp_lse, meta, g_k = 0, g_v = 0;
+    int64_t split_out = 0, split_lse = 0;
     int64_t total;
-    int64_t tmp_rows;   // rows of the continuation temporary
-    int64_t meta_ints;  // int32 elements of metadata
+    int64_t tmp_rows;        // rows of the continuation temporary
+    int64_t meta_ints;       // int32 elements of metadata
+    int64_t split_rows = 0;  // query rows of one split state (the largest split launch)
+    int32_t split_max = 1;   // most splits of any launch
 };
 
 struct Problem {
@@ -107,7 +143,8 @@ int build_problem(const mla_chunked_prefill_params& p, Problem& pb, bool dcp = f
     pb.tokens = qsl[n];
 
     // metadata image: per chunk e_req[n], e_start[n], e_off[n+1], cu_q[n+1]
-    int64_t tmp_rows = 0;
+    int64_t tmp_rows = 0, split_rows = 0;
+    int32_t split_max = 1;
     for (const auto& c : pb.plan.chunks) {
         ChunkMeta m{};
         const int32_t ne = c.num_entries;
@@ -139,6 +176,24 @@ int build_problem(const mla_chunked_prefill_params& p, Problem& pb, bool dcp = f
             }
             m.local_rows = static_cast<int32_t>(loff);
         }
+        // key splits of the chunk's attention launches (see run_chunked)
+        const int32_t first_direct = c.is_continuation ? 1 : 0;
+        if (c.is_continuation && p.query_lens[c.request_begin] > 0) {
+            m.split_cont = plan_split(1, p.query_lens[c.request_begin], pb.plan.lens[c.entry_begin], p.num_heads);
+            if (m.split_cont.splits > 1) {
+                split_rows = std::max<int64_t>(split_rows, p.query_lens[c.request_begin]);
+                split_max = std::max(split_max, m.split_cont.splits);
+            }
+        }
+        if (ne > first_direct) {
+            int32_t max_rows = 0;
+            for (int32_t i = first_direct; i < ne; ++i) max_rows = std::max(max_rows, pb.plan.lens[c.entry_begin + i]);
+            m.split_direct = plan_split(ne - first_direct, c.max_query_len, max_rows, p.num_heads);
+            if (m.split_direct.splits > 1) {
+                split_rows = std::max<int64_t>(split_rows, qsl[c.request_begin + ne] - qsl[c.request_begin]);
+                split_max = std::max(split_max, m.split_direct.splits);
+            }
+        }
         pb.cmeta.push_back(m);
         if (c.is_continuation) tmp_rows = std::max<int64_t>(tmp_rows, p.query_lens[c.request_begin]);
     }
@@ -165,6 +220,12 @@ int build_problem(const mla_chunked_prefill_params& p, Problem& pb, bool dcp = f
     L.tmp_lse = take(H * tmp_rows * 4);
     L.meta_ints = static_cast<int64_t>(pb.meta.size());
     L.meta = take(L.meta_ints * 4);
+    L.split_rows = split_rows;
+    L.split_max = split_max;
+    if (split_max > 1) {
+        L.split_out = take(split_max * split_rows * H * kDv * 2);
+        L.split_lse = take(split_max * H * split_rows * 4);
+    }
     if (dcp) {
         int64_t g_rows = 0;
         for (const auto& m : pb.cmeta) g_rows = std::max<int64_t>(g_rows, static_cast<int64_t>(world) * m.local_rows);
@@ -359,6 +420,43 @@ int run_chunked(const mla_chunked_prefill_params& p, const Problem& pb, hipStrea
         if (b < e) MLA_TRY(launch_init_partial(part_out, part_lse, T, b, e, H, kDv, stream));
     }
 
+    bf16_t* split_out = reinterpret_cast<bf16_t*>(base + L.split_out);
+    float* split_lse = reinterpret_cast<float*>(base + L.split_lse);
+    // Chunk attention of n sequences whose queries are rows [rows_lo, rows_hi)
+    // of the chunk, into dst (LSE head stride dst_stride).  A key-split launch
+    // writes one state per slice, and a merge tree (pairs at distance 1, 2, 4)
+    // folds them into slice 0; its last level writes dst.
+    auto chunk_attn = [&](const bf16_t* qc, const int32_t* cu_q, const int32_t* cu_k, int32_t n, int32_t max_q,
+                          const SplitPlan& sp, int64_t rows_lo, int64_t rows_hi, bf16_t* dst, float* dst_lse,
+                          int64_t dst_stride) -> int {
+        if (sp.splits <= 1)
+            return launch_attention(qc, ws_k, ws_v, cu_q, cu_k, n, max_q, H, p.scale, false, dst, dst_lse, dst_stride,
+                                    stream);
+        const int64_t R = L.split_rows;
+        AttnSplit as;
+        as.splits = sp.splits;
+        as.split_keys = sp.split_keys;
+        as.out_stride = R * H * kDv;
+        as.lse_stride = H * R;
+        MLA_TRY(launch_attention(qc, ws_k, ws_v, cu_q, cu_k, n, max_q, H, p.scale, false, split_out, split_lse, R,
+                                 stream, as));
+        const int64_t rows = rows_hi - rows_lo;
+        auto so = [&](int32_t s) { return split_out + s * as.out_stride + rows_lo * orow; };
+        auto sl = [&](int32_t s) { return split_lse + s * as.lse_stride + rows_lo; };
+        for (int32_t step = 1; step < sp.splits; step *= 2) {
+            const bool last = 2 * step >= sp.splits;
+            for (int32_t s = 0; s + step < sp.splits; s += 2 * step) {
+                if (last)
+                    MLA_TRY(launch_merge(dst + rows_lo * orow, dst_lse + rows_lo, so(0), sl(0), so(step), sl(step), rows,
+                                         H, kDv, dst_stride, R, R, rows, stream));
+                else
+                    MLA_TRY(launch_merge(so(s), sl(s), so(s), sl(s), so(s + step), sl(s + step), rows, H, kDv, R, R, R,
+                                         rows, stream));
+            }
+        }
+        return MLA_OK;
+    };
+
     for (size_t ci = 0; ci < pb.plan.chunks.size(); ++ci) {
         const mla_chunk_desc& c = pb.plan.chunks[ci];
         const ChunkMeta& m = pb.cmeta[ci];
@@ -367,20 +465,21 @@ int run_chunked(const mla_chunked_prefill_params& p, const Problem& pb, hipStrea
         bf16_t* pc = part_out + c.token_begin * orow;
         float* lc = part_lse + c.token_begin;
         int32_t first_direct = 0;
+        int64_t q0 = 0;
         if (c.is_continuation) {
             // the first request already holds the previous chunk's result
-            const int32_t q0 = p.query_lens[c.request_begin];
+            q0 = p.query_lens[c.request_begin];
             if (q0 > 0) {
-                MLA_TRY(launch_attention(qc, ws_k, ws_v, meta + m.cu_q, meta + m.e_off, 1, q0, H, p.scale, false,
-                                         tmp_out, tmp_lse, L.tmp_rows, stream));
+                MLA_TRY(chunk_attn(qc, meta + m.cu_q, meta + m.e_off, 1, static_cast<int32_t>(q0), m.split_cont, 0, q0,
+                                   tmp_out, tmp_lse, L.tmp_rows));
                 MLA_TRY(launch_merge(pc, lc, pc, lc, tmp_out, tmp_lse, q0, H, kDv, T, T, L.tmp_rows, q0, stream));
             }
             first_direct = 1;
         }
         if (c.num_entries > first_direct) {
-            MLA_TRY(launch_attention(qc, ws_k, ws_v, meta + m.cu_q + first_direct, meta + m.e_off + first_direct,
-                                     c.num_entries - first_direct, c.max_query_len, H, p.scale, false, pc, lc, T,
-                                     stream));
+            MLA_TRY(chunk_attn(qc, meta + m.cu_q + first_direct, meta + m.e_off + first_direct,
+                               c.num_entries - first_direct, c.max_query_len, m.split_direct, q0,
+                               c.token_end - c.token_begin, pc, lc, T));
         }
     }
 

@@ -91,9 +91,15 @@ def extra_workloads():
     new tokens each (T = 32768), H = 128, workspace 131072 rows, A = B = 64.
     The equal-window scheduler gives every request with context a 2048-row
     window and needs 64 iterations over the whole batch for the long request;
-    per-request packing needs 2 chunks."""
+    per-request packing needs 2 chunks.
+
+    heterogeneous_h16: the heterogeneous batch (seed-4 lengths) at 16 heads,
+    one GPU's share when its 128 heads are split over 8 GPUs; most of its
+    chunk-attention launches then have fewer workgroups than the GPU has CUs."""
+    c4, q4 = _config4_lens(4)
     return {
         "skewed": Workload("skewed", tuple([131072] + [64] * 63), tuple([512] * 64), 128, 131072, 64, 64, 1.0, 6),
+        "heterogeneous_h16": Workload("heterogeneous_h16", c4, q4, 16, 131072, 64, 64, 1.0, 4),
     }
 
 

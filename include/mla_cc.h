@@ -310,9 +310,9 @@ int mla_chunked_prefill_scratch_size(const mla_chunked_prefill_params* params, i
  * prefix_num_tokens.  Rows of requests without context get their context
  * partial initialised to (0, -inf); a chunk's rows that no earlier chunk wrote
  * are written directly (so a single chunk covering every token needs no
- * partial initialisation or merge).  A chunk-attention launch whose
- * workgroups (requests x 256-query tiles x heads, at most 128 of them) would
- * leave most of the GPU's 256 CUs idle is cut along the key axis instead:
+ * partial initialisation or merge).  A chunk-attention launch whose longest
+ * workgroup (one 256-query tile of one head against a request's rows) would
+ * outlast the average load of the GPU's 256 CUs is cut along the key axis:
  * each request's rows are split into 2..8 slices of at least 4096 rows, one
  * state per slice goes to the scratch, and merge_attn_states folds the slices
  * into the destination rows (exact up to rounding: the merge is the LSE

@@ -22,6 +22,7 @@
 // reorganisation into request order), and the uniform-window scheduler that
 // per-request packing replaced.
 #include <algorithm>
+#include <cmath>
 #include <array>
 #include <cstring>
 #include <map>
@@ -56,13 +57,14 @@ struct VecSink : PlanSink {
 
 // Device metadata of one chunk, as offsets (in int32 elements) into the meta
 // block.  e_lstart / e_loff (local starts and offsets) exist only under DCP.
-// Key split of a chunk-attention launch whose workgroups (sequences x 256-query
-// tiles x heads) cannot fill the GPU's CUs, e.g. one long-context request with
-// few queries, or a head shard of 16 heads per GPU: each sequence's key range
-// is cut into `splits` slices of `split_keys` rows, one workgroup per slice,
-// and the slices' states are LSE-merged (the merge_attn_states operator).
-// Splitting pays only while the split grid still fits in one round of the
-// CUs, and each slice keeps at least kMinSplitTiles key tiles.
+// Key split of a chunk-attention launch whose longest workgroups outlast the
+// average load of a CU, e.g. one long-context request with few queries, or a
+// head shard of 16 heads per GPU: each sequence's key range is cut into
+// `splits` slices of `split_keys` rows, one workgroup per slice, and the
+// slices' states are LSE-merged (the merge_attn_states operator).  The launch
+// takes about max(longest workgroup, total tiles / CUs) tile steps; splitting
+// shortens the first term, so S = ceil(longest / average), while every slice
+// keeps at least kMinSplitTiles key tiles.
 constexpr int32_t kNumCUs = 256;       // MI355X
 constexpr int32_t kMaxSplits = 8;      // the merge tree is at most 3 deep
 constexpr int32_t kMinSplitTiles = 64; // 4096 keys per slice at least
@@ -74,16 +76,26 @@ struct SplitPlan {
     int32_t split_keys = 0;
 };
 
-SplitPlan plan_split(int32_t n_seqs, int32_t max_q, int32_t max_rows, int32_t heads) {
-    const int64_t wgs = static_cast<int64_t>(n_seqs) * ((max_q + kQueryTile - 1) / kQueryTile) * heads;
-    const int32_t key_tiles = (max_rows + kKeyTile - 1) / kKeyTile;
-    if (wgs <= 0) return {};
-    const int64_t s = std::min<int64_t>({kMaxSplits, kNumCUs / wgs, key_tiles / kMinSplitTiles});
+// q_lens / k_rows: the launch's sequences (query rows, key rows)
+SplitPlan plan_split(const int32_t* q_lens, const int32_t* k_rows, int32_t n, int32_t heads) {
+    int64_t work = 0;  // key tiles summed over the launch's live workgroups
+    int32_t longest = 0;
+    for (int32_t i = 0; i < n; ++i) {
+        if (q_lens[i] <= 0) continue;
+        const int32_t kt = (k_rows[i] + kKeyTile - 1) / kKeyTile;
+        work += static_cast<int64_t>((q_lens[i] + kQueryTile - 1) / kQueryTile) * kt * heads;
+        longest = std::max(longest, kt);
+    }
+    if (work <= 0) return {};
+    const double avg = static_cast<double>(work) / kNumCUs;
+    if (longest <= 1.2 * avg) return {};
+    const int64_t s = std::min<int64_t>({kMaxSplits, static_cast<int64_t>(std::ceil(longest / avg)),
+                                         longest / kMinSplitTiles});
     if (s < 2) return {};
     SplitPlan sp;
-    const int32_t tiles = static_cast<int32_t>((key_tiles + s - 1) / s);
+    const int32_t tiles = static_cast<int32_t>((longest + s - 1) / s);
     sp.split_keys = tiles * kKeyTile;
-    sp.splits = (key_tiles + tiles - 1) / tiles;  // no slice starts past the longest range
+    sp.splits = (longest + tiles - 1) / tiles;  // no slice starts past the longest range
     return sp.splits >= 2 ? sp : SplitPlan{};
 }
 
@@ -179,16 +191,15 @@ int build_problem(const mla_chunked_prefill_params& p, Problem& pb, bool dcp = f
         // key splits of the chunk's attention launches (see run_chunked)
         const int32_t first_direct = c.is_continuation ? 1 : 0;
         if (c.is_continuation && p.query_lens[c.request_begin] > 0) {
-            m.split_cont = plan_split(1, p.query_lens[c.request_begin], pb.plan.lens[c.entry_begin], p.num_heads);
+            m.split_cont = plan_split(&p.query_lens[c.request_begin], &pb.plan.lens[c.entry_begin], 1, p.num_heads);
             if (m.split_cont.splits > 1) {
                 split_rows = std::max<int64_t>(split_rows, p.query_lens[c.request_begin]);
                 split_max = std::max(split_max, m.split_cont.splits);
             }
         }
         if (ne > first_direct) {
-            int32_t max_rows = 0;
-            for (int32_t i = first_direct; i < ne; ++i) max_rows = std::max(max_rows, pb.plan.lens[c.entry_begin + i]);
-            m.split_direct = plan_split(ne - first_direct, c.max_query_len, max_rows, p.num_heads);
+            m.split_direct = plan_split(&p.query_lens[c.request_begin + first_direct],
+                                        &pb.plan.lens[c.entry_begin + first_direct], ne - first_direct, p.num_heads);
             if (m.split_direct.splits > 1) {
                 split_rows = std::max<int64_t>(split_rows, qsl[c.request_begin + ne] - qsl[c.request_begin]);
                 split_max = std::max(split_max, m.split_direct.splits);

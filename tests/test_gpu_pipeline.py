@@ -50,17 +50,18 @@ def test_named_small_workloads_full(idx):
         assert np.abs(host(out)[33:164] - sfx).max() <= 2e-2 * 5
 
 
-# Chunk-attention launches with too few workgroups for the GPU (sequences x
-# 256-query tiles x heads <= 128) cut each sequence's key range into slices and
-# LSE-merge the slice states.  Each case's split count follows from
-# min(8, 256 // workgroups, key tiles // 64) and is given in the comment.
+# Chunk-attention launches whose longest workgroup outlasts the average CU load
+# (work = heads x sum of query tiles x key tiles, over 256 CUs) cut each
+# sequence's key range into slices and LSE-merge the slice states.  Each case's
+# split count follows from min(8, ceil(longest / average), longest // 64) key
+# tiles and is given in the comment.
 SPLIT_CASES = [
-    # one chunk, 4 workgroups, 469 key tiles: 7 slices (a merge tree with an odd leaf)
+    # one chunk, 4 workgroups of 469 key tiles: 7 slices (a merge tree with an odd leaf)
     W.Workload("split_single", (30000,), (20,), 4, 32768, 64, 64, 1.0, 501),
     # chunk 0: request 0's first 16384 rows, 4 slices; chunk 1: its continuation
     # (13616 rows) in a launch of its own, 3 slices, then request 1's head
     W.Workload("split_continuation", (30000, 9000, 0), (5, 3, 2), 2, 16384, 64, 64, 1.0, 502),
-    # three sequences in one launch, 24 workgroups, 4 slices of 5056 keys: the
+    # three sequences in one launch, 4 slices of 5056 keys: the
     # shorter sequences' later slices are empty and merge as (0, -inf)
     W.Workload("split_ragged", (20000, 100, 5000), (4, 6, 2), 8, 32768, 64, 64, 1.0, 503),
     # a 16-head shard: 2 query tiles x 16 heads, 4 slices

@@ -125,10 +125,12 @@ def write_traffic(fetch_csv, write_csv, workload, out_path=None):
         out = collections.defaultdict(list)
         for k, v in disp.items():
             n = names[k]
+            if n.startswith("void "):  # function templates demangle with their return type
+                n = n[len("void "):]
             if "neg_kernel" in n:
                 out["calibration"].append(v)
             elif n.startswith("mla::"):
-                short = n.replace("(anonymous namespace)::", "").split("(")[0].split("::")[-1]
+                short = n.replace("(anonymous namespace)::", "").split("(")[0].split("::")[-1].split("<")[0]
                 out[short].append(v)
         return out
 

@@ -197,6 +197,44 @@ inline int32_t gather_rows_per_block(int32_t heads) {
     const int32_t row_vectors = heads * (kDk + kDv) / 8;
     return std::max<int32_t>(1, kGatherThreads * 8 / row_vectors);
 }
+constexpr int kGatherMaxRows = kGatherThreads * 8 / ((kDk + kDv) / 8);  // rows per block at one head
+
+// Copy of `rows` consecutive workspace rows whose cache rows are src_rows[]
+// (-1: write NaN): the rows' K and V vectors form one sequence of
+// rows * (kvec + vvec) vectors, copied kGatherBatch per lane at a time.
+__device__ __forceinline__ void copy_rows(const uint4* __restrict__ k_cache, const uint4* __restrict__ v_cache,
+                                          const int64_t* src_rows, uint4* __restrict__ kdst,
+                                          uint4* __restrict__ vdst, int32_t rows, int kvec, int vvec) {
+    const uint4 nan4 = make_uint4(0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u);
+    const int n = kvec + vvec;
+    const int total = rows * n;
+    for (int base = threadIdx.x; base < total; base += kGatherThreads * kGatherBatch) {
+        uint4 r[kGatherBatch];
+#pragma unroll
+        for (int u = 0; u < kGatherBatch; ++u) {
+            const int idx = base + u * kGatherThreads;
+            r[u] = nan4;
+            if (idx < total) {
+                const int rr = idx / n, v = idx - rr * n;
+                const int64_t src = src_rows[rr];
+                if (src >= 0) r[u] = v < kvec ? load_nt(&k_cache[src * kvec + v]) : load_nt(&v_cache[src * vvec + v - kvec]);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < kGatherBatch; ++u) {
+            const int idx = base + u * kGatherThreads;
+            if (idx < total) {
+                const int rr = idx / n, v = idx - rr * n;
+                const u32x4_t val = {r[u].x, r[u].y, r[u].z, r[u].w};
+                if (v < kvec)
+                    __builtin_nontemporal_store(val, reinterpret_cast<u32x4_t*>(&kdst[static_cast<int64_t>(rr) * kvec + v]));
+                else
+                    __builtin_nontemporal_store(
+                        val, reinterpret_cast<u32x4_t*>(&vdst[static_cast<int64_t>(rr) * vvec + v - kvec]));
+            }
+        }
+    }
+}
 
 // Copy of one workspace row (its K vectors, then its V vectors, as one
 // sequence of kvec + vvec 16-byte vectors): every lane issues up to
@@ -229,6 +267,7 @@ __device__ __forceinline__ void copy_row(const uint4* __restrict__ ksrc, const u
     }
 }
 
+template <bool kMultiRow>
 __global__ __launch_bounds__(kGatherThreads) void gather_kernel(
     const uint4* __restrict__ k_cache, const uint4* __restrict__ v_cache, int64_t num_blocks, int32_t block_size,
     int32_t heads, const int32_t* __restrict__ block_table, int32_t bt_width, const int32_t* __restrict__ e_req,
@@ -244,22 +283,34 @@ __global__ __launch_bounds__(kGatherThreads) void gather_kernel(
     }
     int32_t e = lo;
     const int kvec = heads * (kDk / 8), vvec = heads * (kDv / 8);
-    for (int rr = 0; rr < rows_per_block; ++rr) {
-        const int32_t w = row0 + rr;
-        if (w >= num_rows) break;
+    // cache row of workspace row w (-1: the block table has no valid entry)
+    auto source = [&](int32_t w) -> int64_t {
         while (e + 1 < n_entries && e_off[e + 1] <= w) ++e;
         const int32_t req = e_req[e];
         const int64_t p = static_cast<int64_t>(e_start[e]) + (w - e_off[e]);
         const int64_t lb = p / block_size;
         const int32_t slot = static_cast<int32_t>(p - lb * block_size);
-        bool ok = lb < bt_width && req >= 0;
-        int64_t blk = ok ? block_table[static_cast<int64_t>(req) * bt_width + lb] : 0;
-        ok = ok && blk >= 0 && blk < num_blocks;
-        if (!ok) blk = 0;
-        const int64_t src_row = blk * block_size + slot;
-        copy_row(k_cache + src_row * kvec, v_cache + src_row * vvec, ws_k + static_cast<int64_t>(w) * kvec,
-                 ws_v + static_cast<int64_t>(w) * vvec, kvec, vvec, ok);
+        if (lb >= bt_width || req < 0) return -1;
+        const int64_t blk = block_table[static_cast<int64_t>(req) * bt_width + lb];
+        return blk >= 0 && blk < num_blocks ? blk * block_size + slot : -1;
+    };
+    if (!kMultiRow) {
+        const int64_t src = source(row0);
+        const int64_t s0 = src < 0 ? 0 : src;
+        copy_row(k_cache + s0 * kvec, v_cache + s0 * vvec, ws_k + static_cast<int64_t>(row0) * kvec,
+                 ws_v + static_cast<int64_t>(row0) * vvec, kvec, vvec, src >= 0);
+        return;
     }
+    // several short rows (small head counts): look every row's source up once,
+    // then copy the rows as one sequence of vectors, so that each lane keeps up
+    // to kGatherBatch loads in flight across rows
+    __shared__ int64_t src_rows[kGatherMaxRows];
+    const int32_t rows = min(rows_per_block, num_rows - row0);
+    if (threadIdx.x == 0)
+        for (int32_t rr = 0; rr < rows; ++rr) src_rows[rr] = source(row0 + rr);
+    __syncthreads();
+    copy_rows(k_cache, v_cache, src_rows, ws_k + static_cast<int64_t>(row0) * kvec,
+              ws_v + static_cast<int64_t>(row0) * vvec, rows, kvec, vvec);
 }
 
 // ---------------------------------------------------------- DCP assembly
@@ -388,7 +439,10 @@ int launch_gather(const bf16_t* k_cache, const bf16_t* v_cache, int64_t num_bloc
     const int32_t rows_per_block = gather_rows_per_block(heads);
     const unsigned grid = static_cast<unsigned>((num_rows + rows_per_block - 1) / rows_per_block);
     TimedLaunch timed(MLA_KERNEL_GATHER, stream);
-    hipLaunchKernelGGL(gather_kernel, dim3(grid), dim3(kGatherThreads), 0, stream,
+    // one row per block (large head counts) and several short rows per block
+    // are separate instantiations, so that each keeps its own register count
+    auto kernel = rows_per_block == 1 ? gather_kernel<false> : gather_kernel<true>;
+    hipLaunchKernelGGL(kernel, dim3(grid), dim3(kGatherThreads), 0, stream,
                        reinterpret_cast<const uint4*>(k_cache), reinterpret_cast<const uint4*>(v_cache), num_blocks,
                        block_size, heads, block_table, bt_width, e_req, e_start, e_off, n_entries, num_rows,
                        rows_per_block, reinterpret_cast<uint4*>(ws_k), reinterpret_cast<uint4*>(ws_v));

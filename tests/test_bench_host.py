@@ -8,6 +8,8 @@ import bench
 HEADER = ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"]
 NEG = "void at::native::vectorized_elementwise_kernel<4, at::native::neg_kernel_cuda(at::TensorIteratorBase&)>"
 GATHER = "mla::(anonymous namespace)::gather_kernel(HIP_vector_type<unsigned int, 4u> const*, int)"
+# a function template's instance demangles with its return type and arguments
+GATHER_T = "void mla::(anonymous namespace)::gather_kernel<false>(HIP_vector_type<unsigned int, 4u> const*, int)"
 ATTN = "mla::(anonymous namespace)::chunk_attention_kernel(mla::(anonymous namespace)::AttnArgs)"
 OTHER = "void at::native::vectorized_gather_kernel<16, long>(char*, char*)"
 
@@ -26,9 +28,9 @@ def test_write_traffic_scales_by_the_calibration_copy(tmp_path):
     # the 1 GiB copy reads FETCH_SIZE = 512 Mi KiB units and WRITE_SIZE = 1 Mi:
     # fetch counts 2 bytes per KiB unit read, write 1
     _csv(tmp_path / "f.csv", "FETCH_SIZE",
-         [(1, GATHER, 1000.0), (2, GATHER, 3000.0), (3, ATTN, 500.0), (4, NEG, 524288.0), (5, OTHER, 7.0)])
+         [(1, GATHER, 1000.0), (2, GATHER_T, 3000.0), (3, ATTN, 500.0), (4, NEG, 524288.0), (5, OTHER, 7.0)])
     _csv(tmp_path / "w.csv", "WRITE_SIZE",
-         [(1, GATHER, 2000.0), (2, GATHER, 2000.0), (3, ATTN, 100.0), (4, NEG, 1048576.0), (5, OTHER, 9.0)])
+         [(1, GATHER, 2000.0), (2, GATHER_T, 2000.0), (3, ATTN, 100.0), (4, NEG, 1048576.0), (5, OTHER, 9.0)])
     out = tmp_path / "t.json"
     res = bench.write_traffic(str(tmp_path / "f.csv"), str(tmp_path / "w.csv"), "demo", out_path=str(out))
     assert json.load(open(out)) == res

@@ -314,9 +314,9 @@ int mla_chunked_prefill_scratch_size(const mla_chunked_prefill_params* params, i
  * workgroup (one 256-query tile of one head against a request's rows) would
  * outlast the average load of the GPU's 256 CUs is cut along the key axis:
  * each request's rows are split into 2..8 slices of at least 4096 rows, one
- * state per slice goes to the scratch, and merge_attn_states folds the slices
- * into the destination rows (exact up to rounding: the merge is the LSE
- * combination of disjoint key sets).  Enqueues on `stream`; the host returns
+ * state per slice goes to the scratch, and one merge combines the slices into
+ * the destination rows in fp32 (exact up to rounding: the LSE combination of
+ * disjoint key sets, as merge_attn_states forms it for two).  Enqueues on `stream`; the host returns
  * once the work is enqueued.  Successive calls may overlap: the metadata is
  * staged through pinned host buffers that are recycled only after their copy
  * has completed.

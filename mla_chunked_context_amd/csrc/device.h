@@ -47,6 +47,14 @@ int launch_merge(bf16_t* out, float* out_lse, const bf16_t* p_out, const float* 
                  const float* s_lse, int64_t tokens, int32_t heads, int32_t head_dim, int64_t out_stride,
                  int64_t p_stride, int64_t s_stride, int64_t prefix_num_tokens, hipStream_t stream);
 
+// LSE merge of `slices` (at most kMaxSlices) key-slice states of head_dim 128
+// into out: slice s of token row t is at parts + s * part_stride elements +
+// t * heads * 128 with LSE part_lse[s * lse_slice_stride + h * lse_head_stride + t].
+constexpr int kMaxSlices = 8;
+int launch_merge_slices(bf16_t* out, float* out_lse, int64_t out_lse_stride, const bf16_t* parts,
+                        const float* part_lse, int64_t part_stride, int64_t lse_slice_stride, int64_t lse_head_stride,
+                        int64_t tokens, int32_t heads, int32_t slices, hipStream_t stream);
+
 int launch_gather(const bf16_t* k_cache, const bf16_t* v_cache, int64_t num_blocks, int32_t block_size,
                   int32_t heads, const int32_t* block_table, int32_t bt_width, const int32_t* e_req,
                   const int32_t* e_start, const int32_t* e_off, int32_t n_entries, int32_t num_rows,

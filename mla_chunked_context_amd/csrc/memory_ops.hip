@@ -173,6 +173,67 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel_d128(MergeArgs a) 
     }
 }
 
+// Merge of the key-slice states of one chunk-attention launch (head_dim 128):
+// slice s of (token t, head h) is at parts[s * part_stride + (t * heads + h) *
+// 16] with LSE part_lse[s * lse_slice_stride + h * lse_head_stride + t].  The
+// slices cover disjoint keys, so the result is their LSE combination, formed
+// in fp32 and rounded once.  A slice with LSE -inf (no keys) is not read.
+struct SliceMergeArgs {
+    uint4* out;
+    float* out_lse;
+    int64_t out_lse_stride;
+    const uint4* parts;
+    const float* part_lse;
+    int64_t part_stride;  // 16-byte vectors between slices
+    int64_t lse_slice_stride, lse_head_stride;
+    int64_t tokens;
+    int32_t heads;
+    int32_t slices;
+};
+
+__global__ __launch_bounds__(kMergeThreads) void merge_slices_kernel(SliceMergeArgs a) {
+    const int lane_vec = threadIdx.x & 15;
+    const int64_t row = static_cast<int64_t>(blockIdx.x) * (kMergeThreads / 16) + (threadIdx.x >> 4);
+    if (row >= a.tokens * a.heads) return;
+    const int64_t t = row / a.heads;
+    const int32_t h = static_cast<int32_t>(row - t * a.heads);
+    float l[kMaxSlices];
+    float m = -INFINITY;
+#pragma unroll
+    for (int s = 0; s < kMaxSlices; ++s) {
+        l[s] = s < a.slices ? a.part_lse[s * a.lse_slice_stride + h * a.lse_head_stride + t] : -INFINITY;
+        m = fmaxf(m, l[s]);
+    }
+    uint4 v[kMaxSlices];
+#pragma unroll
+    for (int s = 0; s < kMaxSlices; ++s)
+        if (l[s] != -INFINITY) v[s] = load_nt(&a.parts[s * a.part_stride + row * 16 + lane_vec]);
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    float tot = 0.f;
+#pragma unroll
+    for (int s = 0; s < kMaxSlices; ++s) {
+        if (l[s] == -INFINITY) continue;
+        const float w = expf(l[s] - m);
+        tot += w;
+        const uint32_t wd[4] = {v[s].x, v[s].y, v[s].z, v[s].w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            acc[2 * k] += w * bf16_to_f32(wd[k] & 0xffffu);
+            acc[2 * k + 1] += w * bf16_to_f32(wd[k] >> 16);
+        }
+    }
+    uint4 res = make_uint4(0u, 0u, 0u, 0u);
+    float ol = -INFINITY;
+    if (m != -INFINITY) {
+        const float inv = 1.f / tot;
+        res = make_uint4(pack_bf16x2(acc[0] * inv, acc[1] * inv), pack_bf16x2(acc[2] * inv, acc[3] * inv),
+                         pack_bf16x2(acc[4] * inv, acc[5] * inv), pack_bf16x2(acc[6] * inv, acc[7] * inv));
+        ol = m + logf(tot);
+    }
+    a.out[row * 16 + lane_vec] = res;
+    if (lane_vec == 0) a.out_lse[h * a.out_lse_stride + t] = ol;
+}
+
 // any head_dim that is a multiple of 8
 __global__ __launch_bounds__(kThreads) void merge_kernel_generic(MergeArgs a) {
     const int64_t total = a.tokens * a.heads * a.vec_per_row;
@@ -409,6 +470,20 @@ int launch_init_partial(bf16_t* out, float* lse, int64_t lse_stride, int64_t row
     TimedLaunch timed(MLA_KERNEL_INIT, stream);
     hipLaunchKernelGGL(init_partial_kernel, dim3(grid), dim3(kThreads), 0, stream, o, lse, lse_stride, row_begin,
                        rows, heads, vpt);
+    return hip_status(hipGetLastError());
+}
+
+int launch_merge_slices(bf16_t* out, float* out_lse, int64_t out_lse_stride, const bf16_t* parts,
+                        const float* part_lse, int64_t part_stride, int64_t lse_slice_stride, int64_t lse_head_stride,
+                        int64_t tokens, int32_t heads, int32_t slices, hipStream_t stream) {
+    if (tokens <= 0) return MLA_OK;
+    if (slices < 1 || slices > kMaxSlices || part_stride % 8 != 0) return MLA_ERR_INVALID_ARG;
+    SliceMergeArgs a{reinterpret_cast<uint4*>(out), out_lse, out_lse_stride, reinterpret_cast<const uint4*>(parts),
+                     part_lse, part_stride / 8, lse_slice_stride, lse_head_stride, tokens, heads, slices};
+    const int64_t rows = tokens * heads;
+    const unsigned grid = static_cast<unsigned>((rows + kMergeThreads / 16 - 1) / (kMergeThreads / 16));
+    TimedLaunch timed(MLA_KERNEL_MERGE, stream);
+    hipLaunchKernelGGL(merge_slices_kernel, dim3(grid), dim3(kMergeThreads), 0, stream, a);
     return hip_status(hipGetLastError());
 }
 

@@ -66,7 +66,7 @@ struct VecSink : PlanSink {
 // shortens the first term, so S = ceil(longest / average), while every slice
 // keeps at least kMinSplitTiles key tiles.
 constexpr int32_t kNumCUs = 256;       // MI355X
-constexpr int32_t kMaxSplits = 8;      // the merge tree is at most 3 deep
+constexpr int32_t kMaxSplits = kMaxSlices;  // slices one merge combines
 constexpr int32_t kMinSplitTiles = 64; // 4096 keys per slice at least
 constexpr int32_t kQueryTile = 256;    // queries per attention workgroup
 constexpr int32_t kKeyTile = 64;       // keys per attention tile
@@ -435,8 +435,7 @@ int run_chunked(const mla_chunked_prefill_params& p, const Problem& pb, hipStrea
     float* split_lse = reinterpret_cast<float*>(base + L.split_lse);
     // Chunk attention of n sequences whose queries are rows [rows_lo, rows_hi)
     // of the chunk, into dst (LSE head stride dst_stride).  A key-split launch
-    // writes one state per slice, and a merge tree (pairs at distance 1, 2, 4)
-    // folds them into slice 0; its last level writes dst.
+    // writes one state per slice, and one merge combines them into dst.
     auto chunk_attn = [&](const bf16_t* qc, const int32_t* cu_q, const int32_t* cu_k, int32_t n, int32_t max_q,
                           const SplitPlan& sp, int64_t rows_lo, int64_t rows_hi, bf16_t* dst, float* dst_lse,
                           int64_t dst_stride) -> int {
@@ -451,21 +450,9 @@ int run_chunked(const mla_chunked_prefill_params& p, const Problem& pb, hipStrea
         as.lse_stride = H * R;
         MLA_TRY(launch_attention(qc, ws_k, ws_v, cu_q, cu_k, n, max_q, H, p.scale, false, split_out, split_lse, R,
                                  stream, as));
-        const int64_t rows = rows_hi - rows_lo;
-        auto so = [&](int32_t s) { return split_out + s * as.out_stride + rows_lo * orow; };
-        auto sl = [&](int32_t s) { return split_lse + s * as.lse_stride + rows_lo; };
-        for (int32_t step = 1; step < sp.splits; step *= 2) {
-            const bool last = 2 * step >= sp.splits;
-            for (int32_t s = 0; s + step < sp.splits; s += 2 * step) {
-                if (last)
-                    MLA_TRY(launch_merge(dst + rows_lo * orow, dst_lse + rows_lo, so(0), sl(0), so(step), sl(step), rows,
-                                         H, kDv, dst_stride, R, R, rows, stream));
-                else
-                    MLA_TRY(launch_merge(so(s), sl(s), so(s), sl(s), so(s + step), sl(s + step), rows, H, kDv, R, R, R,
-                                         rows, stream));
-            }
-        }
-        return MLA_OK;
+        return launch_merge_slices(dst + rows_lo * orow, dst_lse + rows_lo, dst_stride, split_out + rows_lo * orow,
+                                   split_lse + rows_lo, as.out_stride, as.lse_stride, R, rows_hi - rows_lo, H,
+                                   sp.splits, stream);
     };
 
     for (size_t ci = 0; ci < pb.plan.chunks.size(); ++ci) {

@@ -56,7 +56,7 @@ def test_named_small_workloads_full(idx):
 # split count follows from min(8, ceil(longest / average), longest // 64) key
 # tiles and is given in the comment.
 SPLIT_CASES = [
-    # one chunk, 4 workgroups of 469 key tiles: 7 slices (a merge tree with an odd leaf)
+    # one chunk, 4 workgroups of 469 key tiles: 7 slices in one merge
     W.Workload("split_single", (30000,), (20,), 4, 32768, 64, 64, 1.0, 501),
     # chunk 0: request 0's first 16384 rows, 4 slices; chunk 1: its continuation
     # (13616 rows) in a launch of its own, 3 slices, then request 1's head

@@ -22,8 +22,8 @@
 // reorganisation into request order), and the uniform-window scheduler that
 // per-request packing replaced.
 #include <algorithm>
-#include <cmath>
 #include <array>
+#include <cmath>
 #include <cstring>
 #include <map>
 #include <mutex>
@@ -55,8 +55,6 @@ struct VecSink : PlanSink {
     int32_t entries_so_far() const override { return static_cast<int32_t>(p->starts.size()); }
 };
 
-// Device metadata of one chunk, as offsets (in int32 elements) into the meta
-// block.  e_lstart / e_loff (local starts and offsets) exist only under DCP.
 // Key split of a chunk-attention launch whose longest workgroups outlast the
 // average load of a CU, e.g. one long-context request with few queries, or a
 // head shard of 16 heads per GPU: each sequence's key range is cut into
@@ -99,6 +97,8 @@ SplitPlan plan_split(const int32_t* q_lens, const int32_t* k_rows, int32_t n, in
     return sp.splits >= 2 ? sp : SplitPlan{};
 }
 
+// Device metadata of one chunk, as offsets (in int32 elements) into the meta
+// block.  e_lstart / e_loff (local starts and offsets) exist only under DCP.
 struct ChunkMeta {
     int64_t e_req, e_start, e_off, cu_q, e_lstart = 0, e_loff = 0;
     int32_t rows = 0;        // context rows (request order)

@@ -107,6 +107,27 @@ def test_dcp_prefill_random_full():
         say("  ", check(host(out), lse.double().cpu().numpy(), ref[0], ref[1], vmax, f"dcp random {seed}"))
 
 
+def test_dcp_prefill_with_key_split():
+    # chunk 0 holds 16384 rows of request 0 against 10 queries at 2 heads: its
+    # attention launch is cut into 4 key slices after the rows are assembled
+    # from the 4 ranks
+    world, il = 4, 1
+    wl = W.Workload("dcp_split", (20000, 3000), (10, 4), 2, 16384, 64, 16, 1.0, 9)
+    say(f"dcp key split world={world} ctx={wl.context_lens} q={wl.query_lens}")
+    b = W.make_batch(wl, device="cpu", canary=True)
+    ranks = W.shard_context(b, world, il)
+    f = W.to_f64
+    ref = O.direct_prefill(f(b.q), f(b.k_new), f(b.v_new), f(b.k_cache), f(b.v_cache), b.block_table.numpy(),
+                           wl.block_size, wl.context_lens, wl.query_lens, wl.scale)
+    d = W.Batch(wl, b.q.to(DEV), b.k_new.to(DEV), b.v_new.to(DEV), b.k_cache.to(DEV), b.v_cache.to(DEV),
+                b.block_table.to(DEV), b.num_blocks, b.spare_blocks)
+    dr = [W.RankCache(r.k_cache.to(DEV), r.v_cache.to(DEV), r.block_table.to(DEV), r.num_blocks, r.context_lens)
+          for r in ranks]
+    out, lse = run_dcp_prefill(mla, d, dr, il)
+    vmax = float(max(np.abs(f(b.v_new)).max(), np.nanmax(np.abs(f(b.v_cache)))))
+    say("  ", check(host(out), lse.double().cpu().numpy(), ref[0], ref[1], vmax, "dcp key split"))
+
+
 def test_dcp_homogeneous_full_size_sampled():
     world, il = 4, 1
 

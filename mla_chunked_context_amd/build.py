@@ -25,6 +25,12 @@ ARCH = "gfx950"
 # no packed-fp32 instructions in device code
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function", f"-I{INCLUDE}", f"-I{CSRC}"]
+# Per-file device flags.  The attention kernels are scheduled for instruction-
+# level parallelism rather than occupancy (they run at a fixed two waves per
+# SIMD): chunk attention measured +0.7% (1224 against 1215 TFLOP/s, twice each
+# on one box).  The kernels then use 218 and 252 of the 256 registers two waves
+# per SIMD allow, with no spills.
+FILE_FLAGS = {"attention.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"]}
 
 
 def _hipcc() -> str:
@@ -38,7 +44,8 @@ def _compile(src: str, hipcc: str, extra) -> str:
     path = os.path.join(CSRC, src)
     obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
     if src.endswith(".hip"):
-        cmd = [hipcc, "-x", "hip", f"--offload-arch={ARCH}", *DEVICE_FLAGS, *COMMON, *extra, "-c", path, "-o", obj]
+        cmd = [hipcc, "-x", "hip", f"--offload-arch={ARCH}", *DEVICE_FLAGS, *FILE_FLAGS.get(src, []), *COMMON, *extra,
+               "-c", path, "-o", obj]
     else:
         cmd = [hipcc, "-x", "c++", *COMMON, *extra, "-c", path, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -105,6 +105,11 @@ def test_heterogeneous_full_size_sampled():
     sampled_check(mla, W.named_workloads()[4], tokens_per_request=4)
 
 
+def test_heterogeneous_h16_full_size_sampled():
+    # one GPU's 16-head share: 7 of its 9 chunk-attention launches split keys
+    sampled_check(mla, W.workload_by_name("heterogeneous_h16"), tokens_per_request=4)
+
+
 def test_long_context_full_size_sampled():
     sampled_check(mla, W.named_workloads()[5], tokens_per_request=8)
 

@@ -2,6 +2,7 @@
 the header declares; the host planner matches the oracle bit for bit; bad
 arguments are rejected before any HIP call."""
 import ctypes
+import math
 import os
 import re
 
@@ -165,6 +166,48 @@ def test_prefill_scratch_size_and_param_checks():
     p.split_alignment = 0
     with pytest.raises(mla.MlaError):
         mla.mla_chunked_prefill_scratch_size(p)
+
+
+def _split_rule(q_lens, k_rows, heads, cus=256):
+    """Key slices of one chunk-attention launch, restated: split when the
+    longest workgroup (one 256-query tile against a sequence's key tiles)
+    exceeds 1.2x the average CU load, into min(8, ceil(longest / average),
+    longest // 64) slices of equal whole tiles."""
+    tiles = [(k + 63) // 64 for q, k in zip(q_lens, k_rows) if q > 0]
+    work = sum((q + 255) // 256 * ((k + 63) // 64) * heads for q, k in zip(q_lens, k_rows) if q > 0)
+    if not tiles or work == 0:
+        return 1
+    longest, avg = max(tiles), work / cus
+    if longest <= 1.2 * avg:
+        return 1
+    s = min(8, math.ceil(longest / avg), longest // 64)
+    if s < 2:
+        return 1
+    per = -(-longest // s)
+    return -(-longest // per)
+
+
+def _scratch(ctx, q, heads, workspace_rows=32768):
+    p = mla.ChunkedPrefillParams()
+    c = np.asarray(ctx, dtype=np.int32)
+    ql = np.asarray(q, dtype=np.int32)
+    p.context_lens, p.query_lens, p.num_requests = c.ctypes.data, ql.ctypes.data, len(ctx)
+    p.num_heads, p.block_size, p.block_table_width, p.num_blocks = heads, 64, 1024, 1024
+    p.scale, p.workspace_rows, p.split_alignment = 0.07, workspace_rows, 64
+    return mla.mla_chunked_prefill_scratch_size(p)
+
+
+@pytest.mark.parametrize("q,heads,ctx_split", [(20, 4, 30000), (300, 16, 20000), (600, 128, 20000), (5, 2, 8192)])
+def test_key_split_scratch_follows_the_split_rule(q, heads, ctx_split):
+    # one request in one chunk either way: only the context length differs, so
+    # the scratch differs by exactly the key-slice states of the split launch,
+    # S x q rows x heads x (256 B output + 4 B LSE), each part 256-byte aligned
+    s = _split_rule([q], [ctx_split], heads)
+    assert _split_rule([q], [3000], heads) == 1
+    diff = _scratch([ctx_split], [q], heads) - _scratch([3000], [q], heads)
+    up = lambda x: -(-x // 256) * 256  # noqa: E731
+    expect = 0 if s == 1 else up(s * q * heads * 256) + up(s * heads * q * 4)
+    assert diff == expect, (s, diff, expect)
 
 
 def test_kernel_kinds_match_header():

@@ -66,6 +66,9 @@ SPLIT_CASES = [
     W.Workload("split_ragged", (20000, 100, 5000), (4, 6, 2), 8, 32768, 64, 64, 1.0, 503),
     # a 16-head shard: 2 query tiles x 16 heads, 4 slices
     W.Workload("split_head_shard", (20000,), (300,), 16, 32768, 64, 64, 1.0, 504),
+    # a request with no new tokens among split sequences: its workgroups exit
+    # at once, the others' 4 slices merge as usual
+    W.Workload("split_zero_query", (20000, 5000, 7000), (4, 0, 3), 4, 32768, 64, 64, 1.0, 505),
 ]
 
 

@@ -26,7 +26,7 @@ Every floating-point step is float64.  Modules:
 from .planner import (ChunkPlan, ContextChunk, ChunkedContextMetadata, aligned_split_len,
                       plan_mla_context_chunks, build_mla_chunked_context_metadata,
                       build_chunked_context)
-from .attention import gather_context_rows, attention_with_lse
+from .attention import gather_context_rows, gather_row_sources, attention_with_lse
 from .merge import (merge_states, merge_attn_states, init_mla_context_partial,
                     accumulate_mla_context_chunk)
 from .pipeline import chunked_prefill, direct_prefill, direct_rows
@@ -36,7 +36,7 @@ from .uniform_window import plan_uniform_windows, uniform_window_prefill, unifor
 __all__ = [
     "ChunkPlan", "ContextChunk", "ChunkedContextMetadata", "aligned_split_len",
     "plan_mla_context_chunks", "build_mla_chunked_context_metadata", "build_chunked_context",
-    "gather_context_rows", "attention_with_lse", "merge_states", "merge_attn_states",
+    "gather_context_rows", "gather_row_sources", "attention_with_lse", "merge_states", "merge_attn_states",
     "init_mla_context_partial", "accumulate_mla_context_chunk", "chunked_prefill",
     "direct_prefill", "direct_rows", "mask_empty_context", "plan_uniform_windows",
     "uniform_window_prefill", "uniform_window_size",

@@ -35,6 +35,22 @@ def gather_context_rows(cache: np.ndarray, block_table: np.ndarray, block_size: 
     return np.concatenate(pieces, axis=0)
 
 
+def gather_row_sources(block_table: np.ndarray, block_size: int, request_ids, starts, seq_lens) -> np.ndarray:
+    """Where each workspace row of one chunk comes from, as a flat cache row
+    index (physical block * block_size + slot), in workspace order: entry i
+    takes positions starts[i] .. starts[i]+seq_lens[i]-1 of request
+    request_ids[i], and position p lives at slot p % B of physical block
+    block_table[r][p // B].  gather_context_rows copies exactly these rows."""
+    pieces = []
+    for r, s, n in zip(request_ids, starts, seq_lens):
+        pos = np.arange(int(s), int(s) + int(n), dtype=np.int64)
+        blocks = np.asarray(block_table)[int(r)][pos // block_size].astype(np.int64)
+        pieces.append(blocks * block_size + pos % block_size)
+    if not pieces:
+        return np.zeros(0, dtype=np.int64)
+    return np.concatenate(pieces)
+
+
 def _attend_one_head(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float):
     """q [nq, dk], k [nk, dk], v [nk, dv] -> out [nq, dv], lse [nq] (fp64)."""
     nq, nk = q.shape[0], k.shape[0]

@@ -86,12 +86,14 @@ def _context_rows_of(cache, block_table, block_size, request, length):
 
 
 def direct_prefill(q, k_new, v_new, k_cache, v_cache, block_table, block_size, context_lens,
-                   query_lens, scale, requests=None):
+                   query_lens, scale, requests=None, query_block=None):
     """The definition computed directly: one softmax per (token, head) over
     the request's context rows followed by its new tokens up to itself.
 
     Returns out [T, H, dv] and lse [H, T] (rows of requests not listed in
-    ``requests`` are left 0 / -inf)."""
+    ``requests`` are left 0 / -inf).  ``query_block`` only bounds memory: a
+    request's tokens are taken that many at a time, each row computed the
+    same way."""
     T, H, dv = q.shape[0], q.shape[1], v_new.shape[2]
     ql = [int(x) for x in query_lens]
     qsl = np.concatenate([[0], np.cumsum(ql)]).astype(np.int64)
@@ -109,15 +111,18 @@ def direct_prefill(q, k_new, v_new, k_cache, v_cache, block_table, block_size, c
         v_all = np.concatenate([vc, np.asarray(v_new[a:b], dtype=np.float64)], axis=0)
         qr = np.asarray(q[a:b], dtype=np.float64)
         key_pos = np.arange(c + n)
-        visible = key_pos[None, :] < (c + 1 + np.arange(n))[:, None]  # [n, c+n]
-        for h in range(H):
-            s = scale * (qr[:, h, :] @ k_all[:, h, :].T)
-            s = np.where(visible, s, -np.inf)
-            m = s.max(axis=1, keepdims=True)
-            e = np.exp(s - m)
-            l = e.sum(axis=1, keepdims=True)
-            out[a:b, h, :] = (e @ v_all[:, h, :]) / l
-            lse[h, a:b] = (m + np.log(l))[:, 0]
+        step = n if query_block is None else int(query_block)
+        for t0 in range(0, n, step):
+            t1 = min(n, t0 + step)
+            visible = key_pos[None, :] < (c + 1 + np.arange(t0, t1))[:, None]  # [t1-t0, c+n]
+            for h in range(H):
+                s = scale * (qr[t0:t1, h, :] @ k_all[:, h, :].T)
+                s = np.where(visible, s, -np.inf)
+                m = s.max(axis=1, keepdims=True)
+                e = np.exp(s - m)
+                l = e.sum(axis=1, keepdims=True)
+                out[a + t0:a + t1, h, :] = (e @ v_all[:, h, :]) / l
+                lse[h, a + t0:a + t1] = (m + np.log(l))[:, 0]
     return out, lse
 
 

@@ -15,7 +15,7 @@ import torch
 import oracle as O
 import oracle.dcp as OD
 import workloads as W
-from tests.gpu_util import check, host, run_dcp_prefill, sampled_check, say
+from tests.gpu_util import check, host, record, run_dcp_prefill, sampled_check, say
 
 pytestmark = pytest.mark.gpu
 
@@ -86,11 +86,22 @@ def test_dcp_prefill_small_full(world, il):
     say("  ", check(host(out), lse.double().cpu().numpy(), ref["out"], ref["lse"], vmax, "dcp small"))
 
 
-def test_dcp_prefill_random_full():
-    for seed in range(8):
+def _random_with_context(count):
+    """The first ``count`` seeded random DCP cases whose batch holds context
+    (a batch without any exercises no rank assembly)."""
+    seed = 0
+    while count > 0:
         world, il = [(2, 1), (4, 1), (2, 2), (8, 1)][seed % 4]
         wl = W.random_workload(seed, max_requests=6, max_ctx=600, max_q=60, heads=(1, 2),
                                alignments=(world * il, 2 * world * il))
+        seed += 1
+        if sum(wl.context_lens) > 0:
+            count -= 1
+            yield seed - 1, world, il, wl
+
+
+def test_dcp_prefill_random_full():
+    for seed, world, il, wl in _random_with_context(8):
         say(f"dcp random seed={seed} world={world} il={il} ctx={wl.context_lens} q={wl.query_lens} "
             f"W={wl.workspace_rows} A={wl.split_alignment} B={wl.block_size}")
         b = W.make_batch(wl, device="cpu", canary=True)
@@ -105,6 +116,29 @@ def test_dcp_prefill_random_full():
         out, lse = run_dcp_prefill(mla, d, dr, il)
         vmax = float(max(np.abs(f(b.v_new)).max(), np.nanmax(np.abs(f(b.v_cache)))))
         say("  ", check(host(out), lse.double().cpu().numpy(), ref[0], ref[1], vmax, f"dcp random {seed}"))
+
+
+def test_dcp_prefill_128_heads_full():
+    # the small DCP batch at 128 heads: one-row gathers per rank, the
+    # reorganisation and the attention at the full head stride, every row
+    world, il = 4, 1
+    wl = W.Workload("dcp_small_h128", SMALL.context_lens, SMALL.query_lens, 128, 512, 64, 16, 1.0, 10)
+    say(f"dcp prefill {wl.name} world={world}")
+    b = W.make_batch(wl, device="cpu", canary=True)
+    ranks = W.shard_context(b, world, il)
+    f = W.to_f64
+    ref = OD.dcp_chunked_prefill(f(b.q), f(b.k_new), f(b.v_new), [f(r.k_cache) for r in ranks],
+                                 [f(r.v_cache) for r in ranks], [r.block_table.numpy() for r in ranks], wl.block_size,
+                                 wl.context_lens, wl.query_lens, wl.workspace_rows, wl.split_alignment, wl.scale,
+                                 world, il)
+    d = W.Batch(wl, b.q.to(DEV), b.k_new.to(DEV), b.v_new.to(DEV), b.k_cache.to(DEV), b.v_cache.to(DEV),
+                b.block_table.to(DEV), b.num_blocks, b.spare_blocks)
+    dr = [W.RankCache(r.k_cache.to(DEV), r.v_cache.to(DEV), r.block_table.to(DEV), r.num_blocks, r.context_lens)
+          for r in ranks]
+    out, lse = run_dcp_prefill(mla, d, dr, il)
+    vmax = float(max(np.abs(f(b.v_new)).max(), np.nanmax(np.abs(f(b.v_cache)))))
+    record(f"dcp {wl.name} every row", check(host(out), lse.double().cpu().numpy(), ref["out"], ref["lse"], vmax,
+                                             wl.name))
 
 
 def test_dcp_prefill_with_key_split():
@@ -128,6 +162,7 @@ def test_dcp_prefill_with_key_split():
     say("  ", check(host(out), lse.double().cpu().numpy(), ref[0], ref[1], vmax, "dcp key split"))
 
 
+@pytest.mark.timeout(600)
 def test_dcp_homogeneous_full_size_sampled():
     world, il = 4, 1
 

@@ -4,10 +4,15 @@ oracle.
 * tiny and empty-context workloads, and random ragged ones: every output row
   and LSE against the oracle's chunked path (which the CPU tests pin to the
   direct definition), with NaN canaries in unused cache slots and scratch;
+* 64- and 128-head batches (the wide-row gather and full head strides):
+  every output row and LSE against the oracle;
 * the full-size workloads, in the same launch configuration the benchmark
-  times: sampled rows (first, last, middle and random tokens of requests; a
-  few heads) against the direct definition computed one row at a time, plus
-  properties that hold at any size (no NaN, finite LSE everywhere).
+  times, with NaN canaries in unused cache slots: sampled rows (first, last,
+  middle and random tokens of every request; a few heads) against the direct
+  definition computed one row at a time, every row of every continuation
+  request and every request without context for a seeded head, plus
+  properties that hold at any size (no NaN, finite LSE everywhere).  Each
+  check asserts the output's relative RMS error as well as its maximum.
 """
 import numpy as np
 import pytest
@@ -15,7 +20,7 @@ import torch
 
 import oracle as O
 import workloads as W
-from tests.gpu_util import check, host, oracle_inputs, run_prefill, sampled_check, say
+from tests.gpu_util import check, host, oracle_inputs, record, run_prefill, sampled_check, say
 
 pytestmark = pytest.mark.gpu
 
@@ -79,6 +84,26 @@ def test_key_split_launches_match_oracle(wl):
     say("  ", res)
 
 
+# Wide head counts run the one-row-per-workgroup gather (at 52 heads and up)
+# and the attention's 64- and 128-head strides; every row is checked.
+WIDE_CASES = [
+    # the tiny workload's lengths at 128 heads: two chunks, one continuation
+    W.Workload("tiny_h128", (768, 512, 512, 0), (3, 5, 7, 4), 128, 1024, 64, 64, 1.0, 601),
+    # 64 heads: request 0's context split over two chunks (chunk 0 holds its
+    # first 8192 rows against 40 queries: 64 workgroups of 128 key tiles, so
+    # the launch is cut into 2 key slices), a request without context, and a
+    # last chunk of its own for request 3
+    W.Workload("ragged_h64", (9000, 70, 0, 700), (40, 300, 5, 2), 64, 8192, 64, 64, 1.0, 602),
+]
+
+
+@pytest.mark.parametrize("wl", WIDE_CASES, ids=[w.name for w in WIDE_CASES])
+def test_wide_head_workloads_full(wl):
+    say(f"pipeline {wl.name} ctx={wl.context_lens} q={wl.query_lens} H={wl.num_heads} W={wl.workspace_rows}")
+    res, *_ = _full_case(wl)
+    record(f"chunked {wl.name} every row", res)
+
+
 def test_random_workloads_full():
     for seed in range(16):
         wl = W.random_workload(seed, max_requests=7, max_ctx=700, max_q=150, heads=(1, 2, 3),
@@ -100,19 +125,23 @@ def test_run_twice_is_bitwise_identical():
 # ------------------------------------------------------------- full sizes
 
 
+@pytest.mark.timeout(600)
 def test_homogeneous_full_size_sampled():
     sampled_check(mla, W.named_workloads()[3])
 
 
+@pytest.mark.timeout(600)
 def test_heterogeneous_full_size_sampled():
     sampled_check(mla, W.named_workloads()[4], tokens_per_request=4)
 
 
+@pytest.mark.timeout(600)
 def test_heterogeneous_h16_full_size_sampled():
     # one GPU's 16-head share: 7 of its 9 chunk-attention launches split keys
     sampled_check(mla, W.workload_by_name("heterogeneous_h16"), tokens_per_request=4)
 
 
+@pytest.mark.timeout(600)
 def test_long_context_full_size_sampled():
     sampled_check(mla, W.named_workloads()[5], tokens_per_request=8)
 
@@ -155,5 +184,6 @@ def test_many_calls_in_flight_reuse_staging_safely():
         assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)) and torch.equal(l1, l2)
 
 
+@pytest.mark.timeout(600)
 def test_skewed_full_size_sampled():
     sampled_check(mla, W.workload_by_name("skewed"), tokens_per_request=3)

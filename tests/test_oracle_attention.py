@@ -48,6 +48,31 @@ def test_gather_is_bit_copy():
     assert (ws[768 + 255] == bits[table[1][255 // 64], 255 % 64]).all()
 
 
+def test_gather_row_sources_by_hand():
+    """Positions 2..8 of a request whose blocks are 5, 9, 2 (4 rows each):
+    slots 2, 3 of block 5, then 0..3 of block 9, then 0 of block 2."""
+    table = np.array([[5, 9, 2]], dtype=np.int32)
+    src = O.gather_row_sources(table, 4, [0], [2], [7])
+    assert src.tolist() == [22, 23, 36, 37, 38, 39, 8]
+    assert O.gather_row_sources(table, 4, [], [], []).size == 0
+
+
+def test_gather_row_sources_are_the_copied_rows():
+    """The index map names exactly the rows the gather copies (tagged cache,
+    several entries, odd starts, block boundaries)."""
+    rng = np.random.default_rng(5)
+    for bs in (1, 4, 16):
+        nb, h, d = 40, 2, 3
+        tag = np.arange(nb * bs * h * d, dtype=np.int64).reshape(nb, bs, h, d)
+        table = np.stack([rng.permutation(nb)[:8] for _ in range(3)]).astype(np.int32)
+        reqs = [2, 0, 1]
+        starts = [int(rng.integers(0, 2 * bs)) for _ in reqs]
+        lens = [int(rng.integers(1, 8 * bs - s + 1)) for s in starts]
+        src = O.gather_row_sources(table, bs, reqs, starts, lens)
+        ws = O.gather_context_rows(tag, table, bs, reqs, starts, lens)
+        assert np.array_equal(tag.reshape(nb * bs, h, d)[src], ws)
+
+
 # ------------------------------------------------------------- attention
 
 

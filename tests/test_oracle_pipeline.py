@@ -154,6 +154,19 @@ def test_pins_catch_missing_threshold(monkeypatch):
     assert not _pins_pass()
 
 
+def test_direct_prefill_query_blocks_only_bound_memory():
+    # blocks of 3 tokens cut requests mid-way; every row is still the definition
+    for seed in (1, 4, 7):
+        wl = W.random_workload(seed, max_ctx=120, max_q=12)
+        a = _arrays(W.make_batch(wl, canary=True))
+        d_out, d_lse = O.direct_prefill(*a, wl.scale)
+        b_out, b_lse = O.direct_prefill(*a, wl.scale, query_block=3)
+        assert np.allclose(b_out, d_out, rtol=0, atol=1e-12)
+        assert np.array_equal(np.isneginf(b_lse), np.isneginf(d_lse))
+        fin = np.isfinite(d_lse)
+        assert np.allclose(b_lse[fin], d_lse[fin], rtol=0, atol=1e-12)
+
+
 def test_direct_rows_matches_direct_prefill():
     wl = W.named_workloads()[1]
     b = W.make_batch(wl)

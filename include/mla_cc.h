@@ -27,7 +27,9 @@
  *     r is in block block_table[r * block_table_width + p / block_size], slot
  *     p % block_size.
  *   - `stream` is a hipStream_t (NULL = the default stream).  Device calls only
- *     enqueue work on it; none synchronises or allocates device memory.
+ *     enqueue work on it and allocate no device memory.  The one host wait is
+ *     in the metadata upload of mla_chunked_prefill, mla_dcp_chunked_prefill
+ *     and mla_uniform_window_prefill (see mla_chunked_prefill).
  *   - An empty attention state is LSE = -inf with output 0.  Merges select
  *     rather than multiply by zero, so the output of an empty side is never
  *     read and may hold garbage or NaN.
@@ -52,6 +54,8 @@ enum {
 #define MLA_QK_HEAD_DIM 192
 #define MLA_V_HEAD_DIM 128
 #define MLA_ABI_VERSION 1
+/* Size of the library's own device scratch used by mla_chunked_prefill_no_alloc (128 MiB per device). */
+#define MLA_NO_ALLOC_SCRATCH_BYTES (128ull << 20)
 
 /* Text of a status code (static storage). */
 const char* mla_status_string(int status);
@@ -318,10 +322,37 @@ int mla_chunked_prefill_scratch_size(const mla_chunked_prefill_params* params, i
  * the destination rows in fp32 (exact up to rounding: the LSE combination of
  * disjoint key sets, as merge_attn_states forms it for two).  Enqueues on `stream`; the host returns
  * once the work is enqueued.  Successive calls may overlap: the metadata is
- * staged through pinned host buffers that are recycled only after their copy
- * has completed.
+ * staged through a ring of 4 pinned host buffers per device, each recycled
+ * only after its copy has completed.  Two host waits follow from this: a call
+ * that finds the next buffer's copy still pending (the fifth call in flight)
+ * waits for that copy, and a buffer that must grow is freed with
+ * hipHostFree (which waits for the device) and reallocated with
+ * hipHostMalloc.  Neither waits for any kernel of the call itself.
  */
 int mla_chunked_prefill(const mla_chunked_prefill_params* params, void* stream);
+
+/*
+ * mla_chunked_prefill for callers that cannot allocate (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation).  Same
+ * params, kernels and result, except:
+ *   - params->scratch and params->scratch_bytes are not read.  The library's
+ *     own device buffer of MLA_NO_ALLOC_SCRATCH_BYTES is used instead: one
+ *     per device, created with the library's code on that device and held
+ *     until the process ends; its address is looked up once per device, on
+ *     the first call there.
+ *   - The chunk metadata is written by small kernels that carry it in their
+ *     arguments: no pinned host memory, no host copy, no host wait.
+ *   - No hipMalloc, hipFree, hipHostMalloc or other allocating HIP or torch
+ *     routine is called (host planning uses ordinary heap memory).
+ * MLA_ERR_CAPACITY when mla_chunked_prefill_scratch_size exceeds
+ * MLA_NO_ALLOC_SCRATCH_BYTES, before any work is enqueued.  Every call on a
+ * device shares that device's buffer, and it keeps the last call's contents
+ * (the path reads nothing it has not written in the same call): calls that
+ * can run at the same time on one device (different streams, or host
+ * threads enqueueing concurrently) race and must not overlap; calls on one
+ * stream are ordered by it and may follow each other freely.
+ */
+int mla_chunked_prefill_no_alloc(const mla_chunked_prefill_params* params, void* stream);
 
 /*
  * The uniform-window context scheduler that per-request packing replaced

@@ -23,6 +23,7 @@ MLA_ERR_UNSUPPORTED = 3
 MLA_ERR_HIP = 4
 QK_HEAD_DIM = 192
 V_HEAD_DIM = 128
+NO_ALLOC_SCRATCH_BYTES = 128 << 20  # MLA_NO_ALLOC_SCRATCH_BYTES
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing: build it first (python mla_chunked_context_amd/build.py)")
@@ -90,6 +91,7 @@ _merge = _sig("mla_merge_attn_states", _ptr, _ptr, _ptr, _ptr, _ptr, _ptr, _i64,
 _mask = _sig("mla_mask_empty_context", _ptr, _i64, _ptr, _i32, _ptr, _ptr, _i32, _i64, _i32, _i32, _ptr)
 _scratch_size = _sig("mla_chunked_prefill_scratch_size", ctypes.POINTER(ChunkedPrefillParams), _i64p)
 _prefill = _sig("mla_chunked_prefill", ctypes.POINTER(ChunkedPrefillParams), _ptr)
+_prefill_no_alloc = _sig("mla_chunked_prefill_no_alloc", ctypes.POINTER(ChunkedPrefillParams), _ptr)
 _plan_dcp = _sig("mla_plan_dcp_context_chunks", _i32p, _i32p, _i32, _i64, _i64, _i32, _i32, _i32,
                  ctypes.POINTER(ChunkDesc), _i32, _i32p, _i32p, _i32p, _i32p, _i32p, _i32, _i32p)
 _dcp_reorg = _sig("mla_dcp_reorganize_context", _ptr, _ptr, _i32, _i32, _i32, _i32, _ptr, _ptr, _ptr, _i32, _i32,
@@ -112,7 +114,7 @@ _timing_read = _sig("mla_kernel_timing_read", ctypes.POINTER(KernelTime))
 EXPORTED = [
     "mla_status_string", "mla_abi_version", "mla_plan_context_chunks", "mla_prefill_token_info",
     "mla_init_context_partial", "mla_gather_context", "mla_context_chunk_attn", "mla_causal_suffix_attn",
-    "mla_merge_attn_states", "mla_chunked_prefill_scratch_size", "mla_chunked_prefill",
+    "mla_merge_attn_states", "mla_chunked_prefill_scratch_size", "mla_chunked_prefill", "mla_chunked_prefill_no_alloc",
     "mla_kernel_timing_enable", "mla_kernel_timing_read", "mla_mask_empty_context", "mla_plan_uniform_windows",
     "mla_uniform_window_prefill_scratch_size", "mla_uniform_window_prefill", "mla_plan_dcp_context_chunks",
     "mla_dcp_reorganize_context", "mla_dcp_chunked_prefill_scratch_size", "mla_dcp_chunked_prefill",
@@ -313,6 +315,11 @@ def mla_chunked_prefill_scratch_size(params: ChunkedPrefillParams) -> int:
 
 def mla_chunked_prefill(params: ChunkedPrefillParams, stream=None):
     _check(_prefill(ctypes.byref(params), _stream(stream)), "mla_chunked_prefill")
+
+
+def mla_chunked_prefill_no_alloc(params: ChunkedPrefillParams, stream=None):
+    """params.scratch is not read: the library's own device buffer is used."""
+    _check(_prefill_no_alloc(ctypes.byref(params), _stream(stream)), "mla_chunked_prefill_no_alloc")
 
 
 def mla_dcp_reorganize_context(gathered_k, gathered_v, world_size, interleave, local_rows, entry_starts,

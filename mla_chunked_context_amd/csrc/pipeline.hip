@@ -32,6 +32,13 @@
 #include "device.h"
 #include "planner.h"
 
+// Scratch of mla_chunked_prefill_no_alloc: a fixed device buffer that every
+// GPU the library runs on holds until the process ends.  Host code never
+// passes this name to a kernel or a copy (on the host it is only a stand-in
+// for the symbol): it uses the per-device address that
+// hipGetSymbolAddress returns (no_alloc_scratch below).
+static __device__ __align__(256) unsigned char scratch[MLA_NO_ALLOC_SCRATCH_BYTES];
+
 namespace mla {
 
 namespace {
@@ -307,6 +314,56 @@ int check_params(const mla_chunked_prefill_params* p) {
     } while (0)
 
 // ---------------------------------------------------------------------------
+// Metadata upload without host staging: the metadata travels in the kernel
+// arguments of small writer launches (kMetaPieceInts int32 each), so the
+// no-allocation entry point needs neither pinned host memory nor a copy
+// from pageable memory.
+
+constexpr int kMetaPieceInts = 480;  // 1920 bytes of arguments per launch
+
+struct MetaPiece {
+    int32_t* dst;
+    int32_t count;
+    int32_t v[kMetaPieceInts];
+};
+
+__global__ __launch_bounds__(512) void write_meta_kernel(MetaPiece piece) {
+    const int i = threadIdx.x;
+    if (i < piece.count) piece.dst[i] = piece.v[i];
+}
+
+int write_meta_args(const int32_t* src, size_t count, int32_t* dst, hipStream_t stream) {
+    for (size_t at = 0; at < count; at += kMetaPieceInts) {
+        MetaPiece piece;
+        piece.dst = dst + at;
+        piece.count = static_cast<int32_t>(std::min<size_t>(kMetaPieceInts, count - at));
+        std::memcpy(piece.v, src + at, static_cast<size_t>(piece.count) * sizeof(int32_t));
+        hipLaunchKernelGGL(write_meta_kernel, dim3(1), dim3(512), 0, stream, piece);
+    }
+    return hip_status(hipGetLastError());
+}
+
+// Device address of `scratch` on each device, looked up once per device
+// (with that device current) on the first no-allocation call there.
+constexpr int kMaxDevices = 64;
+std::mutex g_no_alloc_mu;
+void* g_no_alloc_ptr[kMaxDevices] = {};
+
+int no_alloc_scratch(void** out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return MLA_ERR_HIP;
+    if (dev < 0 || dev >= kMaxDevices) return MLA_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(g_no_alloc_mu);
+    if (g_no_alloc_ptr[dev] == nullptr) {
+        void* ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) return MLA_ERR_HIP;
+        g_no_alloc_ptr[dev] = ptr;
+    }
+    *out = g_no_alloc_ptr[dev];
+    return MLA_OK;
+}
+
+// ---------------------------------------------------------------------------
 // Uniform-window scheduler (the scheduling per-request packing replaced,
 // PR #50613 digest, 功能与动机): every iteration covers the same window of
 // every request and runs attention, mask and merge over the whole batch.
@@ -403,8 +460,10 @@ int check_buffers(const mla_chunked_prefill_params& p, bool needs_cache, int64_t
 
 // The chunk loop shared by the single-device and DCP drivers: `gather`
 // fills the workspace with a chunk's context rows in request order.
-template <class Gather>
-int run_chunked(const mla_chunked_prefill_params& p, const Problem& pb, hipStream_t stream, Gather gather) {
+// `upload_meta(src, ints, dst, stream)` puts the metadata into the scratch.
+template <class Gather, class UploadMeta>
+int run_chunked(const mla_chunked_prefill_params& p, const Problem& pb, hipStream_t stream, Gather gather,
+                UploadMeta upload_meta) {
     const int64_t T = pb.tokens;
     const int32_t H = p.num_heads;
     char* base = static_cast<char*>(p.scratch);
@@ -419,7 +478,7 @@ int run_chunked(const mla_chunked_prefill_params& p, const Problem& pb, hipStrea
     float* tmp_lse = reinterpret_cast<float*>(base + L.tmp_lse);
     int32_t* meta = reinterpret_cast<int32_t*>(base + L.meta);
 
-    MLA_TRY(upload(pb.meta.data(), pb.meta.size() * sizeof(int32_t), meta, stream));
+    MLA_TRY(upload_meta(pb.meta.data(), pb.meta.size(), meta, stream));
 
     const bf16_t* q = static_cast<const bf16_t*>(p.q);
     const int64_t qrow = static_cast<int64_t>(H) * kDk;
@@ -489,6 +548,11 @@ int run_chunked(const mla_chunked_prefill_params& p, const Problem& pb, hipStrea
     return MLA_OK;
 }
 
+// Metadata upload through the pinned staging ring.
+int staged_upload(const int32_t* src, size_t count, int32_t* dst, hipStream_t stream) {
+    return upload(src, count * sizeof(int32_t), dst, stream);
+}
+
 }  // namespace
 
 }  // namespace mla
@@ -519,7 +583,28 @@ int mla_chunked_prefill(const mla_chunked_prefill_params* params, void* stream_v
                              p.num_blocks, p.block_size, H, p.block_table, p.block_table_width, meta + m.e_req,
                              meta + m.e_start, meta + m.e_off, c.num_entries, m.rows, ws_k, ws_v, stream);
     };
-    return run_chunked(p, pb, static_cast<hipStream_t>(stream_v), gather);
+    return run_chunked(p, pb, static_cast<hipStream_t>(stream_v), gather, staged_upload);
+}
+
+int mla_chunked_prefill_no_alloc(const mla_chunked_prefill_params* params, void* stream_v) {
+    using namespace mla;
+    MLA_TRY(check_params(params));
+    Problem pb;
+    MLA_TRY(build_problem(*params, pb));
+    if (pb.tokens == 0) return MLA_OK;
+    if (pb.lay.total > static_cast<int64_t>(MLA_NO_ALLOC_SCRATCH_BYTES)) return MLA_ERR_CAPACITY;
+    mla_chunked_prefill_params p = *params;
+    MLA_TRY(no_alloc_scratch(&p.scratch));
+    p.scratch_bytes = static_cast<int64_t>(MLA_NO_ALLOC_SCRATCH_BYTES);
+    MLA_TRY(check_buffers(p, !pb.plan.chunks.empty(), pb.lay.total));
+    const int32_t H = p.num_heads;
+    auto gather = [&](const mla_chunk_desc& c, const ChunkMeta& m, const int32_t* meta, bf16_t* ws_k, bf16_t* ws_v,
+                      hipStream_t stream) {
+        return launch_gather(static_cast<const bf16_t*>(p.k_cache), static_cast<const bf16_t*>(p.v_cache),
+                             p.num_blocks, p.block_size, H, p.block_table, p.block_table_width, meta + m.e_req,
+                             meta + m.e_start, meta + m.e_off, c.num_entries, m.rows, ws_k, ws_v, stream);
+    };
+    return run_chunked(p, pb, static_cast<hipStream_t>(stream_v), gather, write_meta_args);
 }
 
 int mla_dcp_chunked_prefill_scratch_size(const mla_chunked_prefill_params* params, const mla_dcp_ranks* ranks,
@@ -572,7 +657,7 @@ int mla_dcp_chunked_prefill(const mla_chunked_prefill_params* params, const mla_
         return launch_dcp_reorganize(g_k, g_v, H, D, ranks->interleave, m.local_rows, meta + m.e_start,
                                      meta + m.e_off, meta + m.e_loff, c.num_entries, m.rows, ws_k, ws_v, stream);
     };
-    return run_chunked(p, pb, static_cast<hipStream_t>(stream_v), gather);
+    return run_chunked(p, pb, static_cast<hipStream_t>(stream_v), gather, staged_upload);
 }
 
 }  // extern "C"

@@ -7,6 +7,7 @@ import os
 import re
 
 import numpy as np
+import torch
 import pytest
 
 import oracle as O
@@ -33,6 +34,19 @@ def test_every_declared_symbol_is_exported():
     for n in names:
         assert hasattr(lib, n), n
     assert sorted(mla.EXPORTED) == names
+
+
+def test_no_alloc_prefill_refuses_batches_beyond_its_buffer_before_any_gpu_call():
+    # the homogeneous batch needs 5.6 GB of scratch; the refusal comes from the
+    # host checks, so no device (or device pointer) is involved
+    wl = W.named_workloads()[3]
+    q = torch.empty((wl.num_tokens, wl.num_heads, W.DK), dtype=torch.bfloat16, device="meta")
+    p = mla.make_prefill_params(q, q, q, None, None, None, wl.context_lens, wl.query_lens, wl.workspace_rows,
+                                wl.split_alignment, wl.scale)
+    assert mla.mla_chunked_prefill_scratch_size(p) > mla.NO_ALLOC_SCRATCH_BYTES
+    with pytest.raises(mla.MlaError) as e:
+        mla.mla_chunked_prefill_no_alloc(p, stream=0)  # the default stream: never reached
+    assert e.value.status == mla.MLA_ERR_CAPACITY
 
 
 def test_version_and_status_strings():

@@ -316,11 +316,17 @@ int mla_chunked_prefill_scratch_size(const mla_chunked_prefill_params* params, i
  * are written directly (so a single chunk covering every token needs no
  * partial initialisation or merge).  A chunk-attention launch whose longest
  * workgroup (one 256-query tile of one head against a request's rows) would
- * outlast the average load of the GPU's 256 CUs is cut along the key axis:
+ * outlast the average load of the device's CUs (256 on MI355X) is cut along
+ * the key axis:
  * each request's rows are split into 2..8 slices of at least 4096 rows, one
  * state per slice goes to the scratch, and one merge combines the slices into
  * the destination rows in fp32 (exact up to rounding: the LSE combination of
- * disjoint key sets, as merge_attn_states forms it for two).  Enqueues on `stream`; the host returns
+ * disjoint key sets, as merge_attn_states forms it for two).  The attention
+ * launches are persistent: one workgroup per CU takes (sequence, head, query
+ * tile) items from per-XCD queues, longest sequences first (causal: tile
+ * Q-1-i paired with tile i), and moves on to the other XCDs' queues when its
+ * own is empty; the queues and their counters are part of the uploaded
+ * metadata.  Enqueues on `stream`; the host returns
  * once the work is enqueued.  Successive calls may overlap: the metadata is
  * staged through a ring of 4 pinned host buffers per device, each recycled
  * only after its copy has completed.  Two host waits follow from this: a call

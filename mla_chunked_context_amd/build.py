@@ -19,7 +19,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(PKG, "_build")
 LIB_PATH = os.path.join(PKG, "libmla_cc.so")
 
-SOURCES = ["planner.cpp", "memory_ops.hip", "attention.hip", "pipeline.hip", "timing.hip"]
+SOURCES = ["planner.cpp", "memory_ops.hip", "attention.hip", "pipeline.hip", "timing.hip", "device.hip"]
 
 ARCH = "gfx950"
 # no packed-fp32 instructions in device code

@@ -15,8 +15,13 @@
 //   row-major, V transposed), double-buffered: the next tile's global loads
 //   are in flight while the current tile is computed, and one barrier per
 //   tile separates the write of one buffer from the reads of the other.
-//   Workgroup ids are remapped so that the query tiles of one (sequence, head)
-//   run on the same XCD and share its L2.
+//   The query tiles of one (sequence, head) run on the same XCD and share its
+//   L2.  Two launch forms: one workgroup per tile (workgroup ids remapped so
+//   that the tiles of a (sequence, head) land on one XCD), and a persistent
+//   launch with one workgroup per CU that takes tiles from per-XCD queues,
+//   longest first, and steals from the other XCDs' queues once its own is
+//   empty (XCDs run at slightly different speeds, so equal shares finish at
+//   different times).
 //   K/V tiles are read with buffer loads whose descriptor covers exactly the
 //   valid keys of the tile: keys past the end read as zero without branches,
 //   and are masked to -inf before the softmax.
@@ -40,6 +45,7 @@
 // otherwise the stale m is kept, so p <= 256, which fp32 sums and bf16 P
 // represent with the same relative precision.  The LSE is m + log2(sum)
 // converted to natural log at the end.
+#include <algorithm>
 #include <cmath>
 #include <type_traits>
 
@@ -72,6 +78,7 @@ constexpr int kBufferConfig = 0x00020000;  // dword 3 of a raw buffer descriptor
 constexpr int kWaitVmcnt0 = 0x0F70;
 
 static_assert(kBlockN * kKVecPerRow == kKLoads * kThreads, "K tile must split evenly over threads");
+static_assert(kBlockM == kQueryTileRows, "work queues count query tiles of the kernel's size");
 static_assert(kBlockN / 2 * (kDv / 8) == kThreads, "V tile mapping: 32 key pairs x 16 dim groups");
 
 struct AttnArgs {
@@ -95,6 +102,16 @@ struct AttnArgs {
     int32_t split_keys;
     int64_t split_out_stride;
     int64_t split_lse_stride;
+    int32_t num_xcd;  // XCDs of the device (workgroup b runs on XCD b % num_xcd)
+};
+
+// Work queues of a persistent launch (see WorkQueues in device.h).
+struct QueueArgs {
+    const int32_t* table;
+    int32_t* counters;
+    int32_t num_seqs;
+    int32_t queues;
+    int32_t table_ints;
 };
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
@@ -127,35 +144,37 @@ __device__ __forceinline__ float pair_sum(float x) {
     return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
 }
 
-// Workgroups are dealt to the 8 XCDs round-robin (XCD = bid % 8, and each
+// Workgroups are dealt to the X XCDs round-robin (XCD = bid % X, and each
 // XCD starts its share in bid order).  Logical tiles are (group, q tile) with
-// group = (sequence, head).  XCD x takes groups x, x + 8, x + 16, ... with all
+// group = (sequence, head).  XCD x takes groups x, x + X, x + 2X, ... with all
 // q tiles of a group back to back, so the tiles that stream the same K/V rows
 // run together under one L2, and every sequence's heads are spread evenly
 // over the XCDs whatever the sequence lengths.  Groups past the last full set
-// of 8 keep the identity mapping.
-__device__ __forceinline__ int32_t xcd_logical_tile(int32_t bid, int32_t total, int32_t q_tiles) {
+// of X keep the identity mapping.
+__device__ __forceinline__ int32_t xcd_logical_tile(int32_t bid, int32_t total, int32_t q_tiles, int32_t xcds) {
     const int32_t groups = total / q_tiles;
-    const int32_t full = groups / kNumXcd * kNumXcd;
+    const int32_t full = groups / xcds * xcds;
     if (bid >= full * q_tiles) return bid;
-    const int32_t x = bid % kNumXcd, j = bid / kNumXcd;
-    return (x + kNumXcd * (j / q_tiles)) * q_tiles + j % q_tiles;
+    const int32_t x = bid % xcds, j = bid / xcds;
+    return (x + xcds * (j / q_tiles)) * q_tiles + j % q_tiles;
 }
 
-template <bool kCausal>
-__device__ __forceinline__ void attention_body(const AttnArgs& a, unsigned char* k_lds, bf16_t* vt_lds) {
-    const int32_t tile = xcd_logical_tile(blockIdx.x, a.total_tiles, a.q_tiles);
-    int32_t qt = tile % a.q_tiles;
-    int32_t rest = tile / a.q_tiles;
-    const int32_t split = kCausal ? 0 : rest % a.splits;
-    if (!kCausal) rest /= a.splits;
-    const int32_t head = rest % a.heads;
-    const int32_t seq = rest / a.heads;
-    if (kCausal) qt = a.q_tiles - 1 - qt;  // longest causal tiles first
+// Per-item hook of the tile function: begin() runs first in every item,
+// after_prologue() once the item's first loads have landed and the first
+// barrier has passed (every thread has read the item's coordinates by then).
+struct NoHook {
+    __device__ void begin() {}
+    __device__ void after_prologue() {}
+};
 
+// One tile: 256 queries (tile qt) of sequence seq, head `head`, key slice
+// `split`, against their keys.
+template <bool kCausal, class Hook>
+__device__ __forceinline__ void attention_tile(const AttnArgs& a, int32_t seq, int32_t head, int32_t split,
+                                               int32_t qt, unsigned char* k_lds, bf16_t* vt_lds, Hook& hook) {
+    hook.begin();
     const int32_t q_begin = a.cu_q[seq];
     const int32_t q_len = a.cu_q[seq + 1] - q_begin;
-    if (qt * kBlockM >= q_len) return;
     int32_t k_begin = kCausal ? q_begin : a.cu_k[seq];
     int32_t k_len = kCausal ? q_len : a.cu_k[seq + 1] - k_begin;
     bf16_t* out = a.out;
@@ -224,7 +243,7 @@ __device__ __forceinline__ void attention_body(const AttnArgs& a, unsigned char*
     const int32_t v_goff = 2 * vkp * v_row_bytes + vdc * 16;
     const int v_lpos = vt_pos(2 * vkp);
 
-    u32x4 vreg[kVLoads];
+    u32x4 vreg[kVLoads], vreg1[kVLoads];
     // K(k0 tile) straight into K buffer `buf` (no registers involved)
     auto load_k = [&](int32_t k0, int buf) {
         const int32_t keys = min(kBlockN, kv_end - k0);
@@ -237,14 +256,15 @@ __device__ __forceinline__ void attention_body(const AttnArgs& a, unsigned char*
                 rk, (__attribute__((address_space(3))) void*)(dst + i * 1024), 16, k_goff[i], 0, 0,
                 0);
     };
-    auto load_v = [&](int32_t k0) {
+    auto load_v_into = [&](int32_t k0, u32x4 (&dst)[kVLoads]) {
         const int32_t keys = min(kBlockN, kv_end - k0);
         const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
             const_cast<bf16_t*>(vseq + static_cast<int64_t>(k0) * H * kDv), 0, keys * v_row_bytes, kBufferConfig);
 #pragma unroll
         for (int u = 0; u < kVLoads; ++u)
-            vreg[u] = __builtin_amdgcn_raw_buffer_load_b128(rv, v_goff + u * v_row_bytes, 0, 0);
+            dst[u] = __builtin_amdgcn_raw_buffer_load_b128(rv, v_goff + u * v_row_bytes, 0, 0);
     };
+    auto load_v = [&](int32_t k0) { load_v_into(k0, vreg); };
     auto store_v = [&](int buf) {
         // transpose 2 keys x 8 dims into 8 rows (dims) of 2 keys
         bf16_t* vl = vt_lds + buf * kVtTileElems;
@@ -303,13 +323,15 @@ __device__ __forceinline__ void attention_body(const AttnArgs& a, unsigned char*
     // over V(j-1), then issues K(j+2) straight into K(j)'s buffer and the
     // register loads of V(j+2); both buffers were last read in iteration j-1.
     // The barrier at the end of the iteration publishes them.
+    // Prologue: one round trip.  Q, K(0), K(1) (straight into LDS), V(0) and
+    // V(1) (registers) are all in flight together; V(0) is stored once they
+    // have landed, V(1) at the start of iteration 0.
     f32x16 s_cur[2], s_nxt[2];
     if (n_tiles > 0) {
         load_k(0, 0);
         if (n_tiles > 1) load_k(kBlockN, 1);
         load_v(0);
-        store_v(0);
-        if (n_tiles > 1) load_v(kBlockN);  // V(1): stored at the start of iteration 0
+        if (n_tiles > 1) load_v_into(kBlockN, vreg1);
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // direct-to-LDS loads have landed
     // the same wait as an instruction the compiler sees: the Q fragments'
@@ -317,7 +339,11 @@ __device__ __forceinline__ void attention_body(const AttnArgs& a, unsigned char*
     // prologue's conditional QK leaves a path where they are not, and the loop
     // would otherwise wait for all loads before its first QK MFMA)
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    if (n_tiles > 0) store_v(0);
+#pragma unroll
+    for (int u = 0; u < kVLoads; ++u) vreg[u] = vreg1[u];
     __syncthreads();
+    hook.after_prologue();
     if (n_tiles > 0 && (!kCausal || 0 <= wave_last_q)) qk(s_cur, std::integral_constant<int, 0>{});
     __syncthreads();  // K(0) is overwritten by K(2) at the end of iteration 0
 
@@ -452,28 +478,138 @@ __device__ __forceinline__ void attention_body(const AttnArgs& a, unsigned char*
     }
 }
 
+// Grid form: workgroup bid computes one logical tile.
+template <bool kCausal>
+__device__ __forceinline__ void attention_grid(const AttnArgs& a, unsigned char* k_lds, bf16_t* vt_lds) {
+    const int32_t tile = xcd_logical_tile(blockIdx.x, a.total_tiles, a.q_tiles, a.num_xcd);
+    int32_t qt = tile % a.q_tiles;
+    int32_t rest = tile / a.q_tiles;
+    const int32_t split = kCausal ? 0 : rest % a.splits;
+    if (!kCausal) rest /= a.splits;
+    const int32_t head = rest % a.heads;
+    const int32_t seq = rest / a.heads;
+    if (kCausal) qt = a.q_tiles - 1 - qt;  // longest causal tiles first
+    if (qt * kBlockM >= a.cu_q[seq + 1] - a.cu_q[seq]) return;
+    NoHook hook;
+    attention_tile<kCausal>(a, seq, head, split, qt, k_lds, vt_lds, hook);
+}
+
+// Persistent form.  Thread 0 takes items: one atomic increment of its
+// queue's counter per item, issued when an item begins (so that it lands with
+// the item's first loads) and decoded from the work table in LDS once the
+// item's prologue barrier has passed, into s_next, which every thread reads
+// when the item ends (two barriers later).  A queue whose counter has passed
+// its item count is left for the next one; after all X queues the workgroup
+// ends.  Every workgroup ends after at most (its items + X) increments.
+struct QueueHook {
+    const QueueArgs* w;
+    const int32_t* table;  // LDS copy
+    int32_t* s_next;       // LDS: seq, head, split, qt, qt2 (seq < 0: no more work)
+    int32_t heads, groups;  // H, H * splits
+    bool causal;
+    int32_t queue, tried;   // thread 0's current queue and queues left behind
+    int32_t pending;        // thread 0's in-flight increment result
+
+    // System scope: the increment is performed at memory, past the XCDs'
+    // separate L2s, so every XCD sees one counter (and the zero the upload
+    // wrote before the launch).
+    __device__ int32_t take(int32_t q) {
+        return __hip_atomic_fetch_add(w->counters + q * kCounterStride, 1, __ATOMIC_RELAXED,
+                                      __HIP_MEMORY_SCOPE_SYSTEM);
+    }
+    // item j of the current queue (j may be past its end: move on)
+    __device__ void decode(int32_t j) {
+        const int32_t X = w->queues;
+        for (;;) {
+            int32_t item[5];
+            if (decode_queue_item(table, w->num_seqs, X, groups, heads, causal, queue, j, item)) {
+                for (int k = 0; k < 5; ++k) s_next[k] = item[k];
+                return;
+            }
+            if (++tried >= X) {
+                s_next[0] = -1;
+                return;
+            }
+            queue = (queue + 1) % X;
+            j = take(queue);
+        }
+    }
+    __device__ void begin() {
+        if (threadIdx.x == 0) pending = take(queue);
+    }
+    __device__ void after_prologue() {
+        if (threadIdx.x == 0) decode(pending);
+    }
+};
+
+template <bool kCausal>
+__device__ __forceinline__ void attention_queues(const AttnArgs& a, const QueueArgs& w, unsigned char* k_lds,
+                                                 bf16_t* vt_lds, int32_t* table, int32_t* s_next) {
+    for (int32_t i = threadIdx.x; i < w.table_ints; i += kThreads) table[i] = w.table[i];
+    QueueHook hook;
+    hook.w = &w;
+    hook.table = table;
+    hook.s_next = s_next;
+    hook.heads = a.heads;
+    hook.groups = a.heads * (kCausal ? 1 : a.splits);
+    hook.causal = kCausal;
+    hook.tried = 0;
+    hook.pending = 0;
+    // this workgroup's XCD (hardware register XCC_ID, bits 3:0)
+    hook.queue = static_cast<int32_t>(__builtin_amdgcn_s_getreg((3 << 11) | 20)) % w.queues;
+    __syncthreads();  // the table is in LDS
+    if (threadIdx.x == 0) hook.decode(hook.take(hook.queue));
+    __syncthreads();
+    for (;;) {
+        const int32_t seq = s_next[0], head = s_next[1], split = s_next[2], qt = s_next[3], qt2 = s_next[4];
+        if (seq < 0) break;
+        attention_tile<kCausal>(a, seq, head, split, qt, k_lds, vt_lds, hook);
+        if (kCausal && qt2 >= 0) {
+            NoHook none;
+            attention_tile<kCausal>(a, seq, head, split, qt2, k_lds, vt_lds, none);
+        }
+    }
+}
+
 // Distinct entry points so that profiles separate the two steps.
 __global__ __launch_bounds__(kThreads, 1) void chunk_attention_kernel(AttnArgs a) {
     __shared__ __attribute__((aligned(1024))) unsigned char k_lds[2 * kKTileBytes];
     __shared__ __attribute__((aligned(16))) bf16_t vt_lds[2 * kVtTileElems];
-    attention_body<false>(a, k_lds, vt_lds);
+    attention_grid<false>(a, k_lds, vt_lds);
 }
 
 __global__ __launch_bounds__(kThreads, 1) void suffix_attention_kernel(AttnArgs a) {
     __shared__ __attribute__((aligned(1024))) unsigned char k_lds[2 * kKTileBytes];
     __shared__ __attribute__((aligned(16))) bf16_t vt_lds[2 * kVtTileElems];
-    attention_body<true>(a, k_lds, vt_lds);
+    attention_grid<true>(a, k_lds, vt_lds);
+}
+
+__global__ __launch_bounds__(kThreads, 1) void chunk_attention_queued_kernel(AttnArgs a, QueueArgs w) {
+    __shared__ __attribute__((aligned(1024))) unsigned char k_lds[2 * kKTileBytes];
+    __shared__ __attribute__((aligned(16))) bf16_t vt_lds[2 * kVtTileElems];
+    __shared__ int32_t table[kMaxQueueTableInts];
+    __shared__ int32_t s_next[5];
+    attention_queues<false>(a, w, k_lds, vt_lds, table, s_next);
+}
+
+__global__ __launch_bounds__(kThreads, 1) void suffix_attention_queued_kernel(AttnArgs a, QueueArgs w) {
+    __shared__ __attribute__((aligned(1024))) unsigned char k_lds[2 * kKTileBytes];
+    __shared__ __attribute__((aligned(16))) bf16_t vt_lds[2 * kVtTileElems];
+    __shared__ int32_t table[kMaxQueueTableInts];
+    __shared__ int32_t s_next[5];
+    attention_queues<true>(a, w, k_lds, vt_lds, table, s_next);
 }
 
 }  // namespace
 
-int launch_attention(const bf16_t* q, const bf16_t* k, const bf16_t* v, const int32_t* cu_q, const int32_t* cu_k,
-                     int32_t num_seqs, int32_t max_q, int32_t heads, float scale, bool causal, bf16_t* out,
-                     float* lse, int64_t lse_stride, hipStream_t stream, const AttnSplit& split) {
-    if (num_seqs <= 0 || max_q <= 0) return MLA_OK;
+namespace {
+
+int fill_args(AttnArgs& a, const bf16_t* q, const bf16_t* k, const bf16_t* v, const int32_t* cu_q,
+              const int32_t* cu_k, int32_t num_seqs, int32_t max_q, int32_t heads, float scale, bool causal,
+              bf16_t* out, float* lse, int64_t lse_stride, const AttnSplit& split) {
     if (split.splits < 1 || (split.splits > 1 && (causal || split.split_keys < kBlockN || split.split_keys % kBlockN)))
         return MLA_ERR_INVALID_ARG;
-    AttnArgs a{};
+    a = AttnArgs{};
     a.q = q;
     a.k = k;
     a.v = v;
@@ -489,15 +625,51 @@ int launch_attention(const bf16_t* q, const bf16_t* k, const bf16_t* v, const in
     a.split_keys = split.split_keys;
     a.split_out_stride = split.out_stride;
     a.split_lse_stride = split.lse_stride;
+    a.num_xcd = device_shape().xcds;
     const int64_t total = static_cast<int64_t>(num_seqs) * a.q_tiles * heads * split.splits;
     if (total > INT32_MAX) return MLA_ERR_UNSUPPORTED;
     a.total_tiles = static_cast<int32_t>(total);
     a.scale_log2 = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
+    return MLA_OK;
+}
+
+}  // namespace
+
+int launch_attention(const bf16_t* q, const bf16_t* k, const bf16_t* v, const int32_t* cu_q, const int32_t* cu_k,
+                     int32_t num_seqs, int32_t max_q, int32_t heads, float scale, bool causal, bf16_t* out,
+                     float* lse, int64_t lse_stride, hipStream_t stream, const AttnSplit& split) {
+    if (num_seqs <= 0 || max_q <= 0) return MLA_OK;
+    AttnArgs a;
+    const int st = fill_args(a, q, k, v, cu_q, cu_k, num_seqs, max_q, heads, scale, causal, out, lse, lse_stride,
+                             split);
+    if (st != MLA_OK) return st;
     TimedLaunch timed(causal ? MLA_KERNEL_SUFFIX_ATTN : MLA_KERNEL_CHUNK_ATTN, stream);
     if (causal)
         hipLaunchKernelGGL(suffix_attention_kernel, dim3(a.total_tiles), dim3(kThreads), 0, stream, a);
     else
         hipLaunchKernelGGL(chunk_attention_kernel, dim3(a.total_tiles), dim3(kThreads), 0, stream, a);
+    return hip_status(hipGetLastError());
+}
+
+int launch_attention_persistent(const bf16_t* q, const bf16_t* k, const bf16_t* v, const int32_t* cu_q,
+                                const int32_t* cu_k, int32_t num_seqs, int32_t heads, float scale, bool causal,
+                                bf16_t* out, float* lse, int64_t lse_stride, const WorkQueues& wq,
+                                hipStream_t stream, const AttnSplit& split) {
+    if (num_seqs <= 0 || wq.items <= 0) return MLA_OK;
+    if (wq.queues < 1 || wq.queues > kMaxXcd || wq.num_seqs != num_seqs || wq.table == nullptr ||
+        wq.counters == nullptr || work_table_ints(num_seqs, wq.queues) > kMaxQueueTableInts)
+        return MLA_ERR_INVALID_ARG;
+    AttnArgs a;
+    const int st = fill_args(a, q, k, v, cu_q, cu_k, num_seqs, kBlockM, heads, scale, causal, out, lse, lse_stride,
+                             split);
+    if (st != MLA_OK) return st;
+    QueueArgs w{wq.table, wq.counters, num_seqs, wq.queues, static_cast<int32_t>(work_table_ints(num_seqs, wq.queues))};
+    const int32_t grid = std::min<int32_t>(device_shape().cus, wq.items);
+    TimedLaunch timed(causal ? MLA_KERNEL_SUFFIX_ATTN : MLA_KERNEL_CHUNK_ATTN, stream);
+    if (causal)
+        hipLaunchKernelGGL(suffix_attention_queued_kernel, dim3(grid), dim3(kThreads), 0, stream, a, w);
+    else
+        hipLaunchKernelGGL(chunk_attention_queued_kernel, dim3(grid), dim3(kThreads), 0, stream, a, w);
     return hip_status(hipGetLastError());
 }
 

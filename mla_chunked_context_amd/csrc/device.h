@@ -15,7 +15,18 @@ using bf16_t = uint16_t;  // storage type of bfloat16 tensors (raw bits)
 
 constexpr int kDk = MLA_QK_HEAD_DIM;  // 192
 constexpr int kDv = MLA_V_HEAD_DIM;   // 128
-constexpr int kNumXcd = 8;            // MI355X: 8 XCDs, workgroups dealt round-robin
+constexpr int kMaxXcd = 8;  // most XCDs a device may report here (MI355X has 8)
+
+// Compute units and XCDs of the current device (hipDeviceAttributeMultiprocessorCount
+// and hipDeviceAttributeNumberOfXccs), looked up once per device.  Workgroups are
+// dealt to the XCDs round-robin (workgroup b runs on XCD b % xcds), each XCD with
+// its own L2.  Without a visible device (host-only size queries) this is MI355X's
+// 256 CUs in 8 XCDs.  xcds is clamped to [1, kMaxXcd].
+struct DeviceShape {
+    int32_t cus = 256;
+    int32_t xcds = 8;
+};
+DeviceShape device_shape();
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -79,10 +90,23 @@ struct AttnSplit {
 };
 
 // Varlen attention.  causal: query i of a sequence sees keys 0..i of the same
-// sequence (cu_k must then equal cu_q).
+// sequence (cu_k must then equal cu_q).  One workgroup per (sequence, 256-query
+// tile, head, split); the query tiles of one (sequence, head, split) run on one
+// XCD.
 int launch_attention(const bf16_t* q, const bf16_t* k, const bf16_t* v, const int32_t* cu_q,
                      const int32_t* cu_k, int32_t num_seqs, int32_t max_q, int32_t heads, float scale,
                      bool causal, bf16_t* out, float* lse, int64_t lse_stride, hipStream_t stream,
                      const AttnSplit& split = AttnSplit{});
+
+#include "work_queues.h"
+
+// The same attention as launch_attention, as a persistent launch: one
+// workgroup per CU (at most one per item) takes items from its XCD's queue
+// and then from the other queues, so the launch ends when the work does on
+// every XCD.  Needs work_table_ints(num_seqs, queues) <= kMaxQueueTableInts.
+int launch_attention_persistent(const bf16_t* q, const bf16_t* k, const bf16_t* v, const int32_t* cu_q,
+                                const int32_t* cu_k, int32_t num_seqs, int32_t heads, float scale, bool causal,
+                                bf16_t* out, float* lse, int64_t lse_stride, const WorkQueues& wq,
+                                hipStream_t stream, const AttnSplit& split = AttnSplit{});
 
 }  // namespace mla

@@ -31,16 +31,16 @@ __device__ __forceinline__ uint4 load_nt(const uint4* p) {
     return make_uint4(v[0], v[1], v[2], v[3]);
 }
 
-// Blocks are dealt to the XCDs round-robin.  For a copy whose rows all cost
-// the same, this gives each XCD a contiguous range of block indices instead
-// (blocks past the last full set of kNumXcd keep their own), so the blocks of
-// one XCD stream one contiguous stretch of rows through its L2: the gather
-// measured +6-8%.  Kernels whose work is concentrated in a few rows (the
-// empty-context mask) keep the round-robin spread.  A bijection on
+// Blocks are dealt to the `xcds` XCDs round-robin.  For a copy whose rows all
+// cost the same, this gives each XCD a contiguous range of block indices
+// instead (blocks past the last full set of `xcds` keep their own), so the
+// blocks of one XCD stream one contiguous stretch of rows through its L2: the
+// gather measured +6-8%.  Kernels whose work is concentrated in a few rows
+// (the empty-context mask) keep the round-robin spread.  A bijection on
 // [0, gridDim.x).
-__device__ __forceinline__ int64_t xcd_contiguous_block() {
-    const int64_t b = blockIdx.x, per = gridDim.x / kNumXcd;
-    return b < per * kNumXcd ? (b % kNumXcd) * per + b / kNumXcd : b;
+__device__ __forceinline__ int64_t xcd_contiguous_block(int32_t xcds) {
+    const int64_t b = blockIdx.x, per = gridDim.x / xcds;
+    return b < per * xcds ? (b % xcds) * per + b / xcds : b;
 }
 
 // ---------------------------------------------------------------- init
@@ -333,8 +333,8 @@ __global__ __launch_bounds__(kGatherThreads) void gather_kernel(
     const uint4* __restrict__ k_cache, const uint4* __restrict__ v_cache, int64_t num_blocks, int32_t block_size,
     int32_t heads, const int32_t* __restrict__ block_table, int32_t bt_width, const int32_t* __restrict__ e_req,
     const int32_t* __restrict__ e_start, const int32_t* __restrict__ e_off, int32_t n_entries, int32_t num_rows,
-    int32_t rows_per_block, uint4* __restrict__ ws_k, uint4* __restrict__ ws_v) {
-    const int32_t row0 = static_cast<int32_t>(xcd_contiguous_block()) * rows_per_block;
+    int32_t rows_per_block, int32_t xcds, uint4* __restrict__ ws_k, uint4* __restrict__ ws_v) {
+    const int32_t row0 = static_cast<int32_t>(xcd_contiguous_block(xcds)) * rows_per_block;
     if (row0 >= num_rows) return;
     // entry owning row0: the last i with e_off[i] <= row0 (skips empty entries)
     int32_t lo = 0, hi = n_entries - 1;
@@ -386,9 +386,9 @@ __global__ __launch_bounds__(kGatherThreads) void gather_kernel(
 __global__ __launch_bounds__(kGatherThreads) void dcp_reorganize_kernel(
     const uint4* __restrict__ gk, const uint4* __restrict__ gv, int32_t heads, int32_t world, int32_t il,
     int32_t local_rows, const int32_t* __restrict__ e_start, const int32_t* __restrict__ e_off,
-    const int32_t* __restrict__ e_loff, int32_t n_entries, int32_t num_rows, int32_t rows_per_block,
+    const int32_t* __restrict__ e_loff, int32_t n_entries, int32_t num_rows, int32_t rows_per_block, int32_t xcds,
     uint4* __restrict__ ws_k, uint4* __restrict__ ws_v) {
-    const int32_t row0 = static_cast<int32_t>(xcd_contiguous_block()) * rows_per_block;
+    const int32_t row0 = static_cast<int32_t>(xcd_contiguous_block(xcds)) * rows_per_block;
     if (row0 >= num_rows) return;
     int32_t lo = 0, hi = n_entries - 1;
     while (lo < hi) {
@@ -520,7 +520,8 @@ int launch_gather(const bf16_t* k_cache, const bf16_t* v_cache, int64_t num_bloc
     hipLaunchKernelGGL(kernel, dim3(grid), dim3(kGatherThreads), 0, stream,
                        reinterpret_cast<const uint4*>(k_cache), reinterpret_cast<const uint4*>(v_cache), num_blocks,
                        block_size, heads, block_table, bt_width, e_req, e_start, e_off, n_entries, num_rows,
-                       rows_per_block, reinterpret_cast<uint4*>(ws_k), reinterpret_cast<uint4*>(ws_v));
+                       rows_per_block, device_shape().xcds, reinterpret_cast<uint4*>(ws_k),
+                       reinterpret_cast<uint4*>(ws_v));
     return hip_status(hipGetLastError());
 }
 
@@ -534,7 +535,7 @@ int launch_dcp_reorganize(const bf16_t* gk, const bf16_t* gv, int32_t heads, int
     hipLaunchKernelGGL(dcp_reorganize_kernel, dim3(grid), dim3(kGatherThreads), 0, stream,
                        reinterpret_cast<const uint4*>(gk), reinterpret_cast<const uint4*>(gv), heads, world,
                        interleave, local_rows, e_start, e_off, e_loff, n_entries, num_rows, rows_per_block,
-                       reinterpret_cast<uint4*>(ws_k), reinterpret_cast<uint4*>(ws_v));
+                       device_shape().xcds, reinterpret_cast<uint4*>(ws_k), reinterpret_cast<uint4*>(ws_v));
     return hip_status(hipGetLastError());
 }
 

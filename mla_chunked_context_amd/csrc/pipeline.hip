@@ -69,8 +69,7 @@ struct VecSink : PlanSink {
 // slices' states are LSE-merged (the merge_attn_states operator).  The launch
 // takes about max(longest workgroup, total tiles / CUs) tile steps; splitting
 // shortens the first term, so S = ceil(longest / average), while every slice
-// keeps at least kMinSplitTiles key tiles.
-constexpr int32_t kNumCUs = 256;       // MI355X
+// keeps at least kMinSplitTiles key tiles.  CUs: the device's count.
 constexpr int32_t kMaxSplits = kMaxSlices;  // slices one merge combines
 constexpr int32_t kMinSplitTiles = 64; // 4096 keys per slice at least
 constexpr int32_t kQueryTile = 256;    // queries per attention workgroup
@@ -82,7 +81,7 @@ struct SplitPlan {
 };
 
 // q_lens / k_rows: the launch's sequences (query rows, key rows)
-SplitPlan plan_split(const int32_t* q_lens, const int32_t* k_rows, int32_t n, int32_t heads) {
+SplitPlan plan_split(const int32_t* q_lens, const int32_t* k_rows, int32_t n, int32_t heads, int32_t cus) {
     int64_t work = 0;  // key tiles summed over the launch's live workgroups
     int32_t longest = 0;
     for (int32_t i = 0; i < n; ++i) {
@@ -92,7 +91,7 @@ SplitPlan plan_split(const int32_t* q_lens, const int32_t* k_rows, int32_t n, in
         longest = std::max(longest, kt);
     }
     if (work <= 0) return {};
-    const double avg = static_cast<double>(work) / kNumCUs;
+    const double avg = static_cast<double>(work) / cus;
     if (longest <= 1.2 * avg) return {};
     const int64_t s = std::min<int64_t>({kMaxSplits, static_cast<int64_t>(std::ceil(longest / avg)),
                                          longest / kMinSplitTiles});
@@ -104,6 +103,32 @@ SplitPlan plan_split(const int32_t* q_lens, const int32_t* k_rows, int32_t n, in
     return sp.splits >= 2 ? sp : SplitPlan{};
 }
 
+// Work queues of one persistent attention launch, as offsets (int32
+// elements) into the meta block; table < 0: the launch's table does not fit
+// the kernel's LDS copy and the launch takes one workgroup per tile instead.
+struct QueuePlan {
+    int64_t table = -1, counters = -1;
+    int32_t n = 0, queues = 1, items = 0;
+};
+
+// Appends a launch's work table and its zeroed counters to the meta image
+// (the upload zeroes the counters before every call's launches).
+QueuePlan plan_queues(std::vector<int32_t>& meta, const int32_t* q_lens, const int32_t* k_lens, int32_t n,
+                      int32_t heads, int32_t splits, bool causal, int32_t queues) {
+    QueuePlan qp;
+    if (n <= 0 || work_table_ints(n, queues) > kMaxQueueTableInts) return qp;
+    qp.n = n;
+    qp.queues = queues;
+    qp.table = static_cast<int64_t>(meta.size());
+    meta.resize(meta.size() + work_table_ints(n, queues), 0);
+    const int64_t items = build_work_queues(q_lens, k_lens, n, heads, splits, causal, queues, meta.data() + qp.table);
+    qp.items = static_cast<int32_t>(std::min<int64_t>(items, INT32_MAX));
+    while (meta.size() % kCounterStride) meta.push_back(0);  // each counter on its own 64-byte line
+    qp.counters = static_cast<int64_t>(meta.size());
+    meta.resize(meta.size() + static_cast<size_t>(queues) * kCounterStride, 0);
+    return qp;
+}
+
 // Device metadata of one chunk, as offsets (in int32 elements) into the meta
 // block.  e_lstart / e_loff (local starts and offsets) exist only under DCP.
 struct ChunkMeta {
@@ -112,6 +137,7 @@ struct ChunkMeta {
     int32_t local_rows = 0;  // padded local rows of one rank (DCP)
     SplitPlan split_cont;    // the continuation request's own launch
     SplitPlan split_direct;  // the launch over the other requests
+    QueuePlan queues_cont, queues_direct;
 };
 
 struct Layout {
@@ -129,6 +155,7 @@ struct Problem {
     std::vector<int32_t> meta;  // host image of the device metadata
     std::vector<ChunkMeta> cmeta;
     int64_t suffix_cu;          // offset of the suffix query_start_loc
+    QueuePlan queues_suffix;
     int64_t tokens = 0;
     int32_t max_q = 0;
     int64_t prefix_num_tokens = 0;
@@ -140,6 +167,7 @@ struct Problem {
 int build_problem(const mla_chunked_prefill_params& p, Problem& pb, bool dcp = false, int32_t world = 1,
                   int32_t interleave = 1) {
     const int32_t n = p.num_requests;
+    const DeviceShape shape = device_shape();
     VecSink sink;
     sink.p = &pb.plan;
     pb.world = world;
@@ -198,25 +226,33 @@ int build_problem(const mla_chunked_prefill_params& p, Problem& pb, bool dcp = f
         // key splits of the chunk's attention launches (see run_chunked)
         const int32_t first_direct = c.is_continuation ? 1 : 0;
         if (c.is_continuation && p.query_lens[c.request_begin] > 0) {
-            m.split_cont = plan_split(&p.query_lens[c.request_begin], &pb.plan.lens[c.entry_begin], 1, p.num_heads);
+            m.split_cont = plan_split(&p.query_lens[c.request_begin], &pb.plan.lens[c.entry_begin], 1, p.num_heads,
+                                      shape.cus);
             if (m.split_cont.splits > 1) {
                 split_rows = std::max<int64_t>(split_rows, p.query_lens[c.request_begin]);
                 split_max = std::max(split_max, m.split_cont.splits);
             }
+            m.queues_cont = plan_queues(pb.meta, &p.query_lens[c.request_begin], &pb.plan.lens[c.entry_begin], 1,
+                                        p.num_heads, m.split_cont.splits, false, shape.xcds);
         }
         if (ne > first_direct) {
             m.split_direct = plan_split(&p.query_lens[c.request_begin + first_direct],
-                                        &pb.plan.lens[c.entry_begin + first_direct], ne - first_direct, p.num_heads);
+                                        &pb.plan.lens[c.entry_begin + first_direct], ne - first_direct, p.num_heads,
+                                        shape.cus);
             if (m.split_direct.splits > 1) {
                 split_rows = std::max<int64_t>(split_rows, qsl[c.request_begin + ne] - qsl[c.request_begin]);
                 split_max = std::max(split_max, m.split_direct.splits);
             }
+            m.queues_direct = plan_queues(pb.meta, &p.query_lens[c.request_begin + first_direct],
+                                          &pb.plan.lens[c.entry_begin + first_direct], ne - first_direct, p.num_heads,
+                                          m.split_direct.splits, false, shape.xcds);
         }
         pb.cmeta.push_back(m);
         if (c.is_continuation) tmp_rows = std::max<int64_t>(tmp_rows, p.query_lens[c.request_begin]);
     }
     pb.suffix_cu = static_cast<int64_t>(pb.meta.size());
     for (int32_t r = 0; r <= n; ++r) pb.meta.push_back(static_cast<int32_t>(qsl[r]));
+    pb.queues_suffix = plan_queues(pb.meta, p.query_lens, nullptr, n, p.num_heads, 1, true, shape.xcds);
 
     // scratch layout
     const int64_t H = p.num_heads, T = pb.tokens, W = p.workspace_rows;
@@ -495,20 +531,34 @@ int run_chunked(const mla_chunked_prefill_params& p, const Problem& pb, hipStrea
     // Chunk attention of n sequences whose queries are rows [rows_lo, rows_hi)
     // of the chunk, into dst (LSE head stride dst_stride).  A key-split launch
     // writes one state per slice, and one merge combines them into dst.
+    // attention through the launch's work queues when it has them
+    auto attend = [&](const bf16_t* qa, const bf16_t* ka, const bf16_t* va, const int32_t* cu_q, const int32_t* cu_k,
+                      int32_t n, int32_t max_q, bool causal, bf16_t* dst, float* dst_lse, int64_t dst_stride,
+                      const QueuePlan& qp, const AttnSplit& as) -> int {
+        if (qp.table < 0)
+            return launch_attention(qa, ka, va, cu_q, cu_k, n, max_q, H, p.scale, causal, dst, dst_lse, dst_stride,
+                                    stream, as);
+        WorkQueues wq;
+        wq.table = meta + qp.table;
+        wq.counters = meta + qp.counters;
+        wq.num_seqs = qp.n;
+        wq.queues = qp.queues;
+        wq.items = qp.items;
+        return launch_attention_persistent(qa, ka, va, cu_q, cu_k, n, H, p.scale, causal, dst, dst_lse, dst_stride,
+                                           wq, stream, as);
+    };
     auto chunk_attn = [&](const bf16_t* qc, const int32_t* cu_q, const int32_t* cu_k, int32_t n, int32_t max_q,
                           const SplitPlan& sp, int64_t rows_lo, int64_t rows_hi, bf16_t* dst, float* dst_lse,
-                          int64_t dst_stride) -> int {
+                          int64_t dst_stride, const QueuePlan& qp) -> int {
         if (sp.splits <= 1)
-            return launch_attention(qc, ws_k, ws_v, cu_q, cu_k, n, max_q, H, p.scale, false, dst, dst_lse, dst_stride,
-                                    stream);
+            return attend(qc, ws_k, ws_v, cu_q, cu_k, n, max_q, false, dst, dst_lse, dst_stride, qp, AttnSplit{});
         const int64_t R = L.split_rows;
         AttnSplit as;
         as.splits = sp.splits;
         as.split_keys = sp.split_keys;
         as.out_stride = R * H * kDv;
         as.lse_stride = H * R;
-        MLA_TRY(launch_attention(qc, ws_k, ws_v, cu_q, cu_k, n, max_q, H, p.scale, false, split_out, split_lse, R,
-                                 stream, as));
+        MLA_TRY(attend(qc, ws_k, ws_v, cu_q, cu_k, n, max_q, false, split_out, split_lse, R, qp, as));
         return launch_merge_slices(dst + rows_lo * orow, dst_lse + rows_lo, dst_stride, split_out + rows_lo * orow,
                                    split_lse + rows_lo, as.out_stride, as.lse_stride, R, rows_hi - rows_lo, H,
                                    sp.splits, stream);
@@ -528,7 +578,7 @@ int run_chunked(const mla_chunked_prefill_params& p, const Problem& pb, hipStrea
             q0 = p.query_lens[c.request_begin];
             if (q0 > 0) {
                 MLA_TRY(chunk_attn(qc, meta + m.cu_q, meta + m.e_off, 1, static_cast<int32_t>(q0), m.split_cont, 0, q0,
-                                   tmp_out, tmp_lse, L.tmp_rows));
+                                   tmp_out, tmp_lse, L.tmp_rows, m.queues_cont));
                 MLA_TRY(launch_merge(pc, lc, pc, lc, tmp_out, tmp_lse, q0, H, kDv, T, T, L.tmp_rows, q0, stream));
             }
             first_direct = 1;
@@ -536,13 +586,13 @@ int run_chunked(const mla_chunked_prefill_params& p, const Problem& pb, hipStrea
         if (c.num_entries > first_direct) {
             MLA_TRY(chunk_attn(qc, meta + m.cu_q + first_direct, meta + m.e_off + first_direct,
                                c.num_entries - first_direct, c.max_query_len, m.split_direct, q0,
-                               c.token_end - c.token_begin, pc, lc, T));
+                               c.token_end - c.token_begin, pc, lc, T, m.queues_direct));
         }
     }
 
     const int32_t* scu = meta + pb.suffix_cu;
-    MLA_TRY(launch_attention(q, static_cast<const bf16_t*>(p.k_new), static_cast<const bf16_t*>(p.v_new), scu, scu,
-                             p.num_requests, pb.max_q, H, p.scale, true, suf_out, suf_lse, T, stream));
+    MLA_TRY(attend(q, static_cast<const bf16_t*>(p.k_new), static_cast<const bf16_t*>(p.v_new), scu, scu,
+                   p.num_requests, pb.max_q, true, suf_out, suf_lse, T, pb.queues_suffix, AttnSplit{}));
     MLA_TRY(launch_merge(static_cast<bf16_t*>(p.out), p.out_lse, part_out, part_lse, suf_out, suf_lse, T, H, kDv,
                          T, T, T, pb.prefix_num_tokens, stream));
     return MLA_OK;

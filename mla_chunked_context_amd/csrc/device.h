@@ -8,6 +8,7 @@
 #include <cstdint>
 
 #include "mla_cc.h"
+#include "work_queues.h"
 
 namespace mla {
 
@@ -97,8 +98,6 @@ int launch_attention(const bf16_t* q, const bf16_t* k, const bf16_t* v, const in
                      const int32_t* cu_k, int32_t num_seqs, int32_t max_q, int32_t heads, float scale,
                      bool causal, bf16_t* out, float* lse, int64_t lse_stride, hipStream_t stream,
                      const AttnSplit& split = AttnSplit{});
-
-#include "work_queues.h"
 
 // The same attention as launch_attention, as a persistent launch: one
 // workgroup per CU (at most one per item) takes items from its XCD's queue

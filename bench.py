@@ -98,7 +98,10 @@ def profiled_traffic(kernel, workload):
     return k["fetch_bytes_per_launch"] + k["write_bytes_per_launch"]
 
 
-TRAFFIC_SOURCES = {"chunk_attention_kernel": "attention.hip", "suffix_attention_kernel": "attention.hip"}
+# sources whose hash a kernel's traffic figure is tied to (besides device.h)
+ATTN_SOURCES = ["attention.hip", "work_queues.h"]
+TRAFFIC_SOURCES = {"chunk_attention_kernel": ATTN_SOURCES, "suffix_attention_kernel": ATTN_SOURCES,
+                   "chunk_attention_queued_kernel": ATTN_SOURCES, "suffix_attention_queued_kernel": ATTN_SOURCES}
 
 
 def write_traffic(fetch_csv, write_csv, workload, out_path=None):
@@ -147,8 +150,8 @@ def write_traffic(fetch_csv, write_csv, workload, out_path=None):
     for k in sorted(set(fetch) - {"calibration"}):
         if not write.get(k):
             continue
-        srcs = [f"mla_chunked_context_amd/csrc/{TRAFFIC_SOURCES.get(k, 'memory_ops.hip')}",
-                "mla_chunked_context_amd/csrc/device.h"]
+        srcs = [f"mla_chunked_context_amd/csrc/{f}" for f in TRAFFIC_SOURCES.get(k, ["memory_ops.hip"])] + \
+            ["mla_chunked_context_amd/csrc/device.h"]
         h = hashlib.sha256()
         for src in srcs:
             with open(os.path.join(ROOT, src), "rb") as f:
@@ -165,51 +168,102 @@ def write_traffic(fetch_csv, write_csv, workload, out_path=None):
     return res
 
 
-def cpu_baseline(b, wl, sample_queries, path="chunked", rank_caches=None, dcp=(1, 1)):
-    """The oracle on a bounded sample: head 0 only and the first
-    `sample_queries` new tokens of every request, against full contexts."""
+def host_cpus():
+    """(worker threads, machine CPUs, CPU model) of this host.  Workers: the
+    CPUs this process may run on, capped by OMP_NUM_THREADS when it is set
+    (a GPU machine gives each GPU a share of the host's cores)."""
+    usable = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
+    omp = os.environ.get("OMP_NUM_THREADS")
+    workers = min(usable, int(omp)) if omp and omp.isdigit() and int(omp) > 0 else usable
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return workers, os.cpu_count() or usable, model
+
+
+# default oracle sample per workload: (heads, query tokens per request); None = all
+ORACLE_SAMPLE = {"long_context": ("workers", 2048), "heterogeneous": ("workers", None), "skewed": ("workers", 128)}
+
+
+def cpu_baseline(b, wl, path="chunked", rank_caches=None, dcp=(1, 1), sample_heads=None, sample_queries=None):
+    """The oracle's whole path (fp64 NumPy: plan, gather, context attention,
+    merges, causal suffix, final merge) timed on the host cores.  Work items
+    are heads (the path is independent per head): a pool of one thread per
+    core runs one head's path per item with one BLAS thread each.  Inputs are
+    host copies made before timing (resident, as on the GPU).  Workloads too
+    large to run whole are sampled (a seeded subset of heads and/or the first
+    tokens of every request); the full step's time is then scaled by flops
+    and labelled "extrapolated"."""
     import numpy as np
     import torch
+    from concurrent.futures import ThreadPoolExecutor
+    from threadpoolctl import threadpool_limits
     import oracle
     import workloads as W
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([d.get("num_threads", 1) for d in threadpool_info() if d.get("user_api") == "blas"] or [1])
-    except Exception:  # pragma: no cover
-        cores = os.cpu_count() or 1
+
+    workers, machine_cpus, model = host_cpus()
+    H = wl.num_heads
+    d_heads, d_queries = ORACLE_SAMPLE.get(wl.name, (None, None))
+    if sample_heads is None:
+        sample_heads = min(H, workers) if d_heads == "workers" else H
+    if sample_queries is None:
+        sample_queries = d_queries
+    heads = sorted(int(h) for h in np.random.default_rng(0).choice(H, size=min(H, sample_heads), replace=False))
+    sq = [q if sample_queries is None else min(sample_queries, q) for q in wl.query_lens]
     qsl = np.concatenate([[0], np.cumsum(wl.query_lens)])
-    sq = [min(sample_queries, q) for q in wl.query_lens]
-    idx = np.concatenate([np.arange(qsl[r], qsl[r] + sq[r]) for r in range(wl.num_requests)]).astype(np.int64)
-    it = torch.from_numpy(idx).to(b.q.device)
+    idx = np.concatenate([np.arange(qsl[r], qsl[r] + sq[r]) for r in range(wl.num_requests)] + [np.zeros(0)])
+    it = torch.from_numpy(idx.astype(np.int64)).to(b.q.device)
     f = W.to_f64
-    q = f(b.q.index_select(0, it)[:, 0:1].contiguous())
-    kn = f(b.k_new.index_select(0, it)[:, 0:1].contiguous())
-    vn = f(b.v_new.index_select(0, it)[:, 0:1].contiguous())
-    kc = f(b.k_cache[:, :, 0:1].contiguous())
-    vc = f(b.v_cache[:, :, 0:1].contiguous())
-    bt = b.block_table.cpu().numpy()
+    table = b.block_table.cpu().numpy()
+
+    def inputs(h):
+        hs = slice(h, h + 1)
+        q = f(b.q.index_select(0, it)[:, hs].contiguous())
+        kn = f(b.k_new.index_select(0, it)[:, hs].contiguous())
+        vn = f(b.v_new.index_select(0, it)[:, hs].contiguous())
+        if path == "dcp":
+            return (q, kn, vn, [f(r.k_cache[:, :, hs].contiguous()) for r in rank_caches],
+                    [f(r.v_cache[:, :, hs].contiguous()) for r in rank_caches],
+                    [r.block_table.cpu().numpy() for r in rank_caches])
+        return q, kn, vn, f(b.k_cache[:, :, hs].contiguous()), f(b.v_cache[:, :, hs].contiguous()), table
+
+    per_head = [inputs(h) for h in heads]
+
     if path == "dcp":
-        import oracle.dcp
-        lk = [f(r.k_cache[:, :, 0:1].contiguous()) for r in rank_caches]
-        lv = [f(r.v_cache[:, :, 0:1].contiguous()) for r in rank_caches]
-        lt = [r.block_table.cpu().numpy() for r in rank_caches]
+        import oracle.dcp as odcp
+
+    def run(a):
+        if path == "dcp":
+            odcp.dcp_chunked_prefill(*a, wl.block_size, wl.context_lens, sq, wl.workspace_rows, wl.split_alignment,
+                                     wl.scale, dcp[0], dcp[1])
+        else:
+            fn = oracle.chunked_prefill if path == "chunked" else oracle.uniform_window_prefill
+            fn(*a, wl.block_size, wl.context_lens, sq, wl.workspace_rows, wl.split_alignment, wl.scale)
+
+    with threadpool_limits(limits=1, user_api="blas"):
         t0 = time.perf_counter()
-        oracle.dcp.dcp_chunked_prefill(q, kn, vn, lk, lv, lt, wl.block_size, wl.context_lens, sq, wl.workspace_rows,
-                                       wl.split_alignment, wl.scale, dcp[0], dcp[1])
+        with ThreadPoolExecutor(max_workers=workers) as ex:
+            list(ex.map(run, per_head))
         dt = time.perf_counter() - t0
-    else:
-        run = oracle.chunked_prefill if path == "chunked" else oracle.uniform_window_prefill
-        t0 = time.perf_counter()
-        run(q, kn, vn, kc, vc, bt, wl.block_size, wl.context_lens, sq, wl.workspace_rows, wl.split_alignment,
-            wl.scale)
-        dt = time.perf_counter() - t0
-    flops = FLOP_PER_PAIR * (sum(a * c for a, c in zip(sq, wl.context_lens)) + sum(a * (a + 1) // 2 for a in sq))
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
-            "seconds": round(dt, 3),
-            "sample": f"head 0 of {wl.num_heads}, first {sample_queries} new tokens of each of the "
-                      f"{wl.num_requests} requests against their full contexts (fp64 NumPy, whole {path} "
-                      f"path: plan, gather, context attention, merges, causal suffix); value = sample flops / "
-                      f"time"}
+    pairs = lambda ql: sum(a * c for a, c in zip(ql, wl.context_lens)) + sum(a * (a + 1) // 2 for a in ql)
+    sample_flops = FLOP_PER_PAIR * len(heads) * pairs(sq)
+    full_flops = FLOP_PER_PAIR * H * pairs(wl.query_lens)
+    full = len(heads) == H and sq == list(wl.query_lens)
+    what = (f"all {H} heads" if len(heads) == H else f"{len(heads)} of {H} heads (seeded)") + ", " + \
+        ("all new tokens" if sample_queries is None else f"the first {sample_queries} new tokens of each request")
+    return {"value": sample_flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(workers), "kind": "oracle",
+            "seconds": round(dt, 3), "oracle_ms_per_step": round(dt * full_flops / sample_flops * 1e3, 1),
+            "oracle_ms_kind": "measured" if full else "extrapolated",
+            "machine_cpus": int(machine_cpus), "cpu_model": model,
+            "sample": f"{what}, against full contexts (fp64 NumPy, whole {path} path); a pool of {workers} threads, "
+                      f"one head per item, one BLAS thread each; value = sample flops / time"
+                      + ("" if full else "; oracle_ms_per_step = time x full flops / sample flops")}
 
 
 def mask_cpu_baseline(wl, heads=8):
@@ -250,8 +304,12 @@ def parse():
     ap.add_argument("--path", default="chunked", choices=["chunked", "uniform_window", "mask_empty_context", "dcp"])
     ap.add_argument("--dcp-world", type=int, default=4, help="emulated DCP ranks (--path dcp)")
     ap.add_argument("--dcp-interleave", type=int, default=1, help="DCP interleave run length (--path dcp)")
-    ap.add_argument("--cpu-sample-queries", type=int, default=8192)
+    ap.add_argument("--cpu-sample-queries", type=int, default=None,
+                    help="oracle sample: first N new tokens of each request (default per workload)")
+    ap.add_argument("--cpu-sample-heads", type=int, default=None, help="oracle sample: number of heads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-workloads", action="store_true",
+                    help="skip the per-workload summary that the default run adds")
     ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="host only: write profiles/<workload>_traffic.json from the counter collections of "
                          "rocprofv3 --pmc FETCH_SIZE and --pmc WRITE_SIZE runs of this benchmark, then exit")
@@ -259,6 +317,8 @@ def parse():
                     help="after timing, run one elementwise copy (negation) of this many MiB of bf16 so that "
                          "hardware byte counters can be scaled against a kernel of known traffic")
     args = ap.parse_args()
+    # the default run (no --workload) also reports every named workload
+    args.summary = args.workload is None and args.path == "chunked" and not args.no_workloads
     if args.workload is None:
         args.workload = "long_context" if args.path == "chunked" else "heterogeneous"
     return args
@@ -290,7 +350,7 @@ KIND_WORK = {  # kernel kind -> (work figure, unit, bound)
     "mask": ("mask_bytes", "GB/s", "hbm"), "dcp_reorg": ("reorg_bytes", "GB/s", "hbm"),
     "init": (None, None, "hbm"),
 }
-KIND_KERNEL = {"chunk_attn": "chunk_attention_kernel", "suffix_attn": "suffix_attention_kernel",
+KIND_KERNEL = {"chunk_attn": "chunk_attention_queued_kernel", "suffix_attn": "suffix_attention_queued_kernel",
                "gather": "gather_kernel", "merge": "merge_kernel_d128", "mask": "mask_empty_context_kernel",
                "dcp_reorg": "dcp_reorganize_kernel", "init": "init_partial_kernel"}
 
@@ -331,6 +391,44 @@ def roofline(kt, wf, K, workload, kind=None):
     else:
         r["algorithmic_bytes_per_launch"] = per_launch
     return r
+
+
+def workload_summary(mla, torch, W, args, res):
+    """Every named workload on the chunked path: step latency and kernel
+    rates (10 timed steps after 2 warm-ups) beside the oracle's time for the
+    same step on the host cores."""
+    out = {}
+    dev = "cuda:0"
+    for idx, wl in W.named_workloads().items():
+        if wl.name == args.workload:
+            e = {"ms_per_step": res["ms_per_step"], "kernels": res["kernels"]}
+            if "cpu_baseline" in res:
+                e["cpu_oracle"] = res["cpu_baseline"]
+            out[wl.name] = e
+            continue
+        log(f"bench: summary of {wl.name}")
+        b = W.make_batch(wl, device=dev, canary=False)
+        T, H = wl.num_tokens, wl.num_heads
+        o = torch.empty((T, H, W.DV), dtype=torch.bfloat16, device=dev)
+        l = torch.empty((H, T), dtype=torch.float32, device=dev)
+        mk = lambda s=None: mla.make_prefill_params(  # noqa: E731
+            b.q, b.k_new, b.v_new, b.k_cache, b.v_cache, b.block_table, wl.context_lens, wl.query_lens,
+            wl.workspace_rows, wl.split_alignment, wl.scale, out=o, out_lse=l, scratch=s)
+        scratch = torch.empty(max(256, mla.mla_chunked_prefill_scratch_size(mk())), dtype=torch.uint8, device=dev)
+        p = mk(scratch)
+        chunks, _, _ = mla.mla_plan_context_chunks(wl.context_lens, wl.query_lens, wl.workspace_rows, 0,
+                                                   wl.split_alignment)
+        ms, kt = timed_steps(mla, torch, lambda: mla.mla_chunked_prefill(p), 10, 2)
+        e = {"ms_per_step": round(ms, 4), "kernels": kernel_table(kt, work_figures(wl, chunks), 10),
+             "tokens": T, "context_rows": sum(wl.context_lens), "num_heads": H, "chunks": len(chunks)}
+        del scratch
+        if not args.no_cpu_baseline:
+            log(f"bench: oracle on {wl.name}")
+            e["cpu_oracle"] = cpu_baseline(b, wl)
+        out[wl.name] = e
+        del b, o, l
+        torch.cuda.empty_cache()
+    return out
 
 
 def main():
@@ -460,9 +558,13 @@ def main():
         if args.path == "mask_empty_context":
             res["cpu_baseline"] = mask_cpu_baseline(wl)
         else:
-            res["cpu_baseline"] = cpu_baseline(b, wl, args.cpu_sample_queries, args.path,
-                                               rank_caches if args.path == "dcp" else None,
-                                               (args.dcp_world, args.dcp_interleave))
+            res["cpu_baseline"] = cpu_baseline(b, wl, args.path, rank_caches if args.path == "dcp" else None,
+                                               (args.dcp_world, args.dcp_interleave), args.cpu_sample_heads,
+                                               args.cpu_sample_queries)
+    if args.summary:
+        del b
+        torch.cuda.empty_cache()
+        res["workloads"] = workload_summary(mla, torch, W, args, res)
     print(json.dumps(res), flush=True)
 
 

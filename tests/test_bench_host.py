@@ -43,3 +43,16 @@ def test_write_traffic_scales_by_the_calibration_copy(tmp_path):
     assert k["chunk_attention_kernel"]["fetch_bytes_per_launch"] == 500 * 1024 * 2
     assert k["chunk_attention_kernel"]["sources"][0].endswith("attention.hip")
     assert k["gather_kernel"]["sources"][0].endswith("memory_ops.hip")
+
+
+def test_cpu_baseline_reports_host_and_labels_extrapolation():
+    import workloads as W
+    wl = W.named_workloads()[1]
+    b = W.make_batch(wl, canary=False)
+    full = bench.cpu_baseline(b, wl)
+    assert full["kind"] == "oracle" and full["oracle_ms_kind"] == "measured"
+    assert full["cores"] >= 1 and full["machine_cpus"] >= full["cores"] and full["cpu_model"]
+    assert abs(full["oracle_ms_per_step"] - full["seconds"] * 1e3) < 1.0  # both rounded
+    part = bench.cpu_baseline(b, wl, sample_heads=2, sample_queries=3)
+    assert part["oracle_ms_kind"] == "extrapolated" and "2 of 8 heads" in part["sample"]
+    assert part["oracle_ms_per_step"] > part["seconds"] * 1e3

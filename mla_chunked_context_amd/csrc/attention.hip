@@ -168,10 +168,14 @@ struct NoHook {
 };
 
 // One tile: 256 queries (tile qt) of sequence seq, head `head`, key slice
-// `split`, against their keys.
+// `split`, against their keys.  reverse (causal only): key tiles are taken
+// last to first.  The softmax does not depend on the order, and a causal
+// wave's first active tile in that order holds the keys at its own positions,
+// so none of its queries meets the tile with every key masked.
 template <bool kCausal, class Hook>
 __device__ __forceinline__ void attention_tile(const AttnArgs& a, int32_t seq, int32_t head, int32_t split,
-                                               int32_t qt, unsigned char* k_lds, bf16_t* vt_lds, Hook& hook) {
+                                               int32_t qt, bool reverse, unsigned char* k_lds, bf16_t* vt_lds,
+                                               Hook& hook) {
     hook.begin();
     const int32_t q_begin = a.cu_q[seq];
     const int32_t q_len = a.cu_q[seq + 1] - q_begin;
@@ -278,6 +282,8 @@ __device__ __forceinline__ void attention_tile(const AttnArgs& a, int32_t seq, i
     };
 
     const int32_t n_tiles = (kv_end + kBlockN - 1) / kBlockN;
+    // first key of the tile taken at step j
+    auto key0 = [&](int32_t j) { return (kCausal && reverse ? n_tiles - 1 - j : j) * kBlockN; };
     const int32_t wave_first_q = qt * kBlockM + wave * kQPerWave;
     const int32_t wave_last_q = wave_first_q + kQPerWave - 1;
     // per-lane LDS bases; every fragment read is base + a compile-time offset
@@ -328,10 +334,10 @@ __device__ __forceinline__ void attention_tile(const AttnArgs& a, int32_t seq, i
     // have landed, V(1) at the start of iteration 0.
     f32x16 s_cur[2], s_nxt[2];
     if (n_tiles > 0) {
-        load_k(0, 0);
-        if (n_tiles > 1) load_k(kBlockN, 1);
-        load_v(0);
-        if (n_tiles > 1) load_v_into(kBlockN, vreg1);
+        load_k(key0(0), 0);
+        if (n_tiles > 1) load_k(key0(1), 1);
+        load_v(key0(0));
+        if (n_tiles > 1) load_v_into(key0(1), vreg1);
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // direct-to-LDS loads have landed
     // the same wait as an instruction the compiler sees: the Q fragments'
@@ -344,18 +350,18 @@ __device__ __forceinline__ void attention_tile(const AttnArgs& a, int32_t seq, i
     for (int u = 0; u < kVLoads; ++u) vreg[u] = vreg1[u];
     __syncthreads();
     hook.after_prologue();
-    if (n_tiles > 0 && (!kCausal || 0 <= wave_last_q)) qk(s_cur, std::integral_constant<int, 0>{});
+    if (n_tiles > 0 && (!kCausal || key0(0) <= wave_last_q)) qk(s_cur, std::integral_constant<int, 0>{});
     __syncthreads();  // K(0) is overwritten by K(2) at the end of iteration 0
 
     auto step = [&](int32_t j, auto par_tag) {
         constexpr int par = decltype(par_tag)::value;  // j & 1
-        const int32_t k0 = j * kBlockN;
+        const int32_t k0 = key0(j);
         // V(j+1) over V(j-1); K(j+2) straight into the buffer that held K(j).
         // Both were last read in iteration j-1, before the previous barrier.
         if (j + 1 < n_tiles) store_v(par ^ 1);
         if (j + 2 < n_tiles) {
-            load_k(k0 + 2 * kBlockN, par);
-            load_v(k0 + 2 * kBlockN);  // stored at the start of iteration j+1
+            load_k(key0(j + 2), par);
+            load_v(key0(j + 2));  // stored at the start of iteration j+1
         }
         const bool active = !kCausal || k0 <= wave_last_q;  // a causal wave past this tile skips it
 
@@ -377,7 +383,7 @@ __device__ __forceinline__ void attention_tile(const AttnArgs& a, int32_t seq, i
             // on the last tile they read the other K buffer's stale (in-bounds)
             // contents and the result is never used.
             if (kCausal) {
-                if (j + 1 < n_tiles && k0 + kBlockN <= wave_last_q)
+                if (j + 1 < n_tiles && key0(j + 1) <= wave_last_q)
                     qk(s_nxt, std::integral_constant<int, par ^ 1>{});
             } else {
                 qk(s_nxt, std::integral_constant<int, par ^ 1>{});
@@ -491,7 +497,7 @@ __device__ __forceinline__ void attention_grid(const AttnArgs& a, unsigned char*
     if (kCausal) qt = a.q_tiles - 1 - qt;  // longest causal tiles first
     if (qt * kBlockM >= a.cu_q[seq + 1] - a.cu_q[seq]) return;
     NoHook hook;
-    attention_tile<kCausal>(a, seq, head, split, qt, k_lds, vt_lds, hook);
+    attention_tile<kCausal>(a, seq, head, split, qt, false, k_lds, vt_lds, hook);
 }
 
 // Persistent form.  Thread 0 takes items: one atomic increment of its
@@ -563,10 +569,14 @@ __device__ __forceinline__ void attention_queues(const AttnArgs& a, const QueueA
     for (;;) {
         const int32_t seq = s_next[0], head = s_next[1], split = s_next[2], qt = s_next[3], qt2 = s_next[4];
         if (seq < 0) break;
-        attention_tile<kCausal>(a, seq, head, split, qt, k_lds, vt_lds, hook);
+        attention_tile<kCausal>(a, seq, head, split, qt, false, k_lds, vt_lds, hook);
         if (kCausal && qt2 >= 0) {
+            // the pair's short tile runs its keys last to first: the group's
+            // long tiles read key block tau at time tau and its short tiles
+            // block Q - tau, so a group's workgroups share two key blocks at a
+            // time in L2 instead of spreading over all of them
             NoHook none;
-            attention_tile<kCausal>(a, seq, head, split, qt2, k_lds, vt_lds, none);
+            attention_tile<kCausal>(a, seq, head, split, qt2, true, k_lds, vt_lds, none);
         }
     }
 }

@@ -104,6 +104,34 @@ def test_wide_head_workloads_full(wl):
     record(f"chunked {wl.name} every row", res)
 
 
+@pytest.mark.parametrize("rate", [0.3, -0.3, 0.03])
+def test_suffix_pairs_with_rising_and_falling_scores(rate):
+    # requests without context, so the prefill output is the causal suffix
+    # alone: 700 and 1100 new tokens (3 and 5 query tiles: pairs (2, 0) and
+    # (4, 0), (3, 1), a lone middle tile) whose scores rise (or fall) by about
+    # rate * 40 log2 units per 64-key tile, so the running max of the tile
+    # taken last-to-first moves the other way
+    say(f"suffix pairs, score slope {rate}")
+    g = torch.Generator().manual_seed(41)
+    ql, H = (700, 1100), 2
+    T = sum(ql)
+    u = 2.0 * torch.randn(H, W.DK, generator=g)
+    pos = torch.cat([torch.arange(n) for n in ql])
+    q = (u[None] + torch.randn(T, H, W.DK, generator=g)).to(torch.bfloat16)
+    k = ((pos // 64).float()[:, None, None] * rate * u[None] + torch.randn(T, H, W.DK, generator=g)).to(torch.bfloat16)
+    v = torch.randn(T, H, W.DV, generator=g).to(torch.bfloat16)
+    kc = torch.full((1, 64, H, W.DK), float("nan")).to(torch.bfloat16)
+    vc = torch.full((1, 64, H, W.DV), float("nan")).to(torch.bfloat16)
+    wl = W.Workload("suffix_pairs", (0, 0), ql, H, 256, 64, 64, 1.0, 0)
+    bt = torch.zeros((2, 1), dtype=torch.int32)
+    d = W.Batch(wl, q.to(DEV), k.to(DEV), v.to(DEV), kc.to(DEV), vc.to(DEV), bt.to(DEV), 1)
+    out, lse = run_prefill(mla, d)
+    ref_o, ref_l = O.direct_prefill(host(q), host(k), host(v), host(kc), host(vc), bt.numpy(), 64, (0, 0), ql,
+                                    wl.scale)
+    record(f"suffix pairs slope {rate}", check(host(out), lse.double().cpu().numpy(), ref_o, ref_l,
+                                               float(np.abs(host(v)).max()), f"slope {rate}"))
+
+
 def test_random_workloads_full():
     for seed in range(16):
         wl = W.random_workload(seed, max_requests=7, max_ctx=700, max_q=150, heads=(1, 2, 3),

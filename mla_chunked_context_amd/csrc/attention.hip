@@ -168,10 +168,11 @@ struct NoHook {
 };
 
 // One tile: 256 queries (tile qt) of sequence seq, head `head`, key slice
-// `split`, against their keys.  reverse (causal only): key tiles are taken
-// last to first.  The softmax does not depend on the order, and a causal
-// wave's first active tile in that order holds the keys at its own positions,
-// so none of its queries meets the tile with every key masked.
+// `split`, against their keys.  Causal tiles take the key tiles below their
+// diagonal block first and the diagonal ones last; reverse takes the former
+// last to first.  The softmax does not depend on the order, and every query
+// has unmasked keys in its wave's first active tile (below the diagonal, or
+// key tile 0).
 template <bool kCausal, class Hook>
 __device__ __forceinline__ void attention_tile(const AttnArgs& a, int32_t seq, int32_t head, int32_t split,
                                                int32_t qt, bool reverse, unsigned char* k_lds, bf16_t* vt_lds,
@@ -283,7 +284,12 @@ __device__ __forceinline__ void attention_tile(const AttnArgs& a, int32_t seq, i
 
     const int32_t n_tiles = (kv_end + kBlockN - 1) / kBlockN;
     // first key of the tile taken at step j
-    auto key0 = [&](int32_t j) { return (kCausal && reverse ? n_tiles - 1 - j : j) * kBlockN; };
+    // Causal: key tiles that end past the tile's first query meet its diagonal
+    // block (the last n_tiles - n_plain in key order, n_plain a multiple of 4).
+    // The others are taken first, in key order or, when reverse, last to first;
+    // the diagonal tiles follow in key order.
+    const int32_t n_plain = kCausal ? min(n_tiles, qt * kBlockM / kBlockN) : n_tiles;
+    auto key0 = [&](int32_t j) { return (kCausal && reverse && j < n_plain ? n_plain - 1 - j : j) * kBlockN; };
     const int32_t wave_first_q = qt * kBlockM + wave * kQPerWave;
     const int32_t wave_last_q = wave_first_q + kQPerWave - 1;
     // per-lane LDS bases; every fragment read is base + a compile-time offset
@@ -353,8 +359,13 @@ __device__ __forceinline__ void attention_tile(const AttnArgs& a, int32_t seq, i
     if (n_tiles > 0 && (!kCausal || key0(0) <= wave_last_q)) qk(s_cur, std::integral_constant<int, 0>{});
     __syncthreads();  // K(0) is overwritten by K(2) at the end of iteration 0
 
-    auto step = [&](int32_t j, auto par_tag) {
+    // kDiag: the tile meets the diagonal block of a causal query tile (some of
+    // its keys lie past some of the tile's queries).  Every other tile runs
+    // the plain step: all waves active, no causal mask, and the same basic
+    // block structure as the non-causal kernel.
+    auto step = [&](int32_t j, auto par_tag, auto diag_tag) {
         constexpr int par = decltype(par_tag)::value;  // j & 1
+        constexpr bool kDiag = kCausal && decltype(diag_tag)::value;
         const int32_t k0 = key0(j);
         // V(j+1) over V(j-1); K(j+2) straight into the buffer that held K(j).
         // Both were last read in iteration j-1, before the previous barrier.
@@ -363,16 +374,16 @@ __device__ __forceinline__ void attention_tile(const AttnArgs& a, int32_t seq, i
             load_k(key0(j + 2), par);
             load_v(key0(j + 2));  // stored at the start of iteration j+1
         }
-        const bool active = !kCausal || k0 <= wave_last_q;  // a causal wave past this tile skips it
+        const bool active = !kDiag || k0 <= wave_last_q;  // a causal wave past this tile skips it
 
         // ---- mask keys of S(j) past the end (and above the diagonal when causal)
-        if (active && ((k0 + kBlockN > kv_end) || (kCausal && k0 + kBlockN - 1 > wave_first_q))) {
+        if (active && ((k0 + kBlockN > kv_end) || (kDiag && k0 + kBlockN - 1 > wave_first_q))) {
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int32_t key = k0 + kb * 32 + (r >> 2) * 8 + g * 4 + (r & 3);
-                    const bool dead = key >= kv_end || (kCausal && key > q_row);
+                    const bool dead = key >= kv_end || (kDiag && key > q_row);
                     if (dead) s_cur[kb][r] = -INFINITY;
                 }
         }
@@ -382,7 +393,7 @@ __device__ __forceinline__ void attention_tile(const AttnArgs& a, int32_t seq, i
             // that they share a basic block with the neighbouring VALU work;
             // on the last tile they read the other K buffer's stale (in-bounds)
             // contents and the result is never used.
-            if (kCausal) {
+            if (kDiag) {
                 if (j + 1 < n_tiles && key0(j + 1) <= wave_last_q)
                     qk(s_nxt, std::integral_constant<int, par ^ 1>{});
             } else {
@@ -460,10 +471,19 @@ __device__ __forceinline__ void attention_tile(const AttnArgs& a, int32_t seq, i
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) s_cur[kb] = s_nxt[kb];
     };
-    for (int32_t j = 0; j < n_tiles; j += 2) {
-        step(j, std::integral_constant<int, 0>{});
-        if (j + 1 < n_tiles) step(j + 1, std::integral_constant<int, 1>{});
-    }
+    // The plain tiles run the plain step, the diagonal ones the causal step,
+    // each in a loop of its own taking steps in pairs (n_plain is even).
+    using P0 = std::integral_constant<int, 0>;
+    using P1 = std::integral_constant<int, 1>;
+    int32_t j = 0;
+    auto run = [&](int32_t j_end, auto diag_tag) {
+        for (; j < j_end; j += 2) {
+            step(j, P0{}, diag_tag);
+            if (j + 1 < j_end) step(j + 1, P1{}, diag_tag);
+        }
+    };
+    run(n_plain, std::false_type{});
+    if (kCausal) run(n_tiles, std::true_type{});
 
     // ---- epilogue: normalise, write bf16 output rows and the LSE
     const float l_tot = pair_sum(l_run);
@@ -515,6 +535,7 @@ struct QueueHook {
     bool causal;
     int32_t queue, tried;   // thread 0's current queue and queues left behind
     int32_t pending;        // thread 0's in-flight increment result
+    bool enabled;           // takes the next item in this tile (the first tile of an item)
 
     // System scope: the increment is performed at memory, past the XCDs'
     // separate L2s, so every XCD sees one counter (and the zero the upload
@@ -541,10 +562,10 @@ struct QueueHook {
         }
     }
     __device__ void begin() {
-        if (threadIdx.x == 0) pending = take(queue);
+        if (enabled && threadIdx.x == 0) pending = take(queue);
     }
     __device__ void after_prologue() {
-        if (threadIdx.x == 0) decode(pending);
+        if (enabled && threadIdx.x == 0) decode(pending);
     }
 };
 
@@ -561,6 +582,7 @@ __device__ __forceinline__ void attention_queues(const AttnArgs& a, const QueueA
     hook.causal = kCausal;
     hook.tried = 0;
     hook.pending = 0;
+    hook.enabled = true;
     // this workgroup's XCD (hardware register XCC_ID, bits 3:0)
     hook.queue = static_cast<int32_t>(__builtin_amdgcn_s_getreg((3 << 11) | 20)) % w.queues;
     __syncthreads();  // the table is in LDS
@@ -569,14 +591,15 @@ __device__ __forceinline__ void attention_queues(const AttnArgs& a, const QueueA
     for (;;) {
         const int32_t seq = s_next[0], head = s_next[1], split = s_next[2], qt = s_next[3], qt2 = s_next[4];
         if (seq < 0) break;
-        attention_tile<kCausal>(a, seq, head, split, qt, false, k_lds, vt_lds, hook);
-        if (kCausal && qt2 >= 0) {
-            // the pair's short tile runs its keys last to first: the group's
-            // long tiles read key block tau at time tau and its short tiles
-            // block Q - tau, so a group's workgroups share two key blocks at a
-            // time in L2 instead of spreading over all of them
-            NoHook none;
-            attention_tile<kCausal>(a, seq, head, split, qt2, true, k_lds, vt_lds, none);
+        // a causal pair's short tile runs its keys below the diagonal last to
+        // first: the group's long tiles read key block tau at time tau and its
+        // short tiles block Q - tau, so a group's workgroups share two key
+        // blocks at a time in L2 instead of spreading over all of them.  One
+        // call site for both tiles keeps one copy of the tile code.
+        const int32_t n_items = kCausal && qt2 >= 0 ? 2 : 1;
+        for (int32_t t = 0; t < n_items; ++t) {
+            hook.enabled = t == 0;
+            attention_tile<kCausal>(a, seq, head, split, t == 0 ? qt : qt2, t == 1, k_lds, vt_lds, hook);
         }
     }
 }

@@ -62,7 +62,7 @@ int launch_merge(bf16_t* out, float* out_lse, const bf16_t* p_out, const float* 
 // LSE merge of `slices` (at most kMaxSlices) key-slice states of head_dim 128
 // into out: slice s of token row t is at parts + s * part_stride elements +
 // t * heads * 128 with LSE part_lse[s * lse_slice_stride + h * lse_head_stride + t].
-constexpr int kMaxSlices = 8;
+constexpr int kMaxSlices = 16;
 int launch_merge_slices(bf16_t* out, float* out_lse, int64_t out_lse_stride, const bf16_t* parts,
                         const float* part_lse, int64_t part_stride, int64_t lse_slice_stride, int64_t lse_head_stride,
                         int64_t tokens, int32_t heads, int32_t slices, hipStream_t stream);

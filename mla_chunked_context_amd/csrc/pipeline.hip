@@ -66,19 +66,68 @@ struct VecSink : PlanSink {
 // average load of a CU, e.g. one long-context request with few queries, or a
 // head shard of 16 heads per GPU: each sequence's key range is cut into
 // `splits` slices of `split_keys` rows, one workgroup per slice, and the
-// slices' states are LSE-merged (the merge_attn_states operator).  The launch
-// takes about max(longest workgroup, total tiles / CUs) tile steps; splitting
-// shortens the first term, so S = ceil(longest / average), while every slice
-// keeps at least kMinSplitTiles key tiles.  CUs: the device's count.
+// slices' states are LSE-merged (the merge_attn_states operator).
+// The persistent launch deals its workgroups longest first to whichever CU
+// frees up, so its length is that of list scheduling in that order.  Among
+// S = 1 .. kMaxSplits slices of at least kMinSplitTiles key tiles each, the
+// split with the shortest simulated schedule is taken (a longer split only
+// if it gains kSplitGain), each workgroup costing its key tiles plus
+// kItemOverheadTiles.  Launches whose longest workgroup stays within 1.2x
+// the average CU load are not split.  CUs: the device's count.
 constexpr int32_t kMaxSplits = kMaxSlices;  // slices one merge combines
 constexpr int32_t kMinSplitTiles = 64; // 4096 keys per slice at least
 constexpr int32_t kQueryTile = 256;    // queries per attention workgroup
 constexpr int32_t kKeyTile = 64;       // keys per attention tile
+constexpr int64_t kItemOverheadTiles = 1;
+constexpr double kSplitGain = 0.97;
+constexpr int64_t kMaxSimulatedItems = 1 << 16;
 
 struct SplitPlan {
     int32_t splits = 1;
     int32_t split_keys = 0;
 };
+
+// Length in tile steps of list scheduling `cus` CUs over the workgroups of
+// a launch cut into slices of `slice_tiles` key tiles (0: no split), in
+// longest-first order; -1 past kMaxSimulatedItems workgroups.
+int64_t simulated_length(const int32_t* q_lens, const int32_t* k_rows, int32_t n, int32_t heads, int32_t cus,
+                         int32_t slices, int32_t slice_tiles) {
+    std::vector<std::pair<int64_t, int64_t>> classes;  // (cost, count)
+    int64_t items = 0;
+    for (int32_t i = 0; i < n; ++i) {
+        if (q_lens[i] <= 0) continue;
+        const int64_t kt = (k_rows[i] + kKeyTile - 1) / kKeyTile;
+        const int64_t per_slice = static_cast<int64_t>((q_lens[i] + kQueryTile - 1) / kQueryTile) * heads;
+        for (int32_t s = 0; s < slices; ++s) {
+            const int64_t c = slices == 1 ? kt : std::max<int64_t>(0, std::min<int64_t>(kt - s * slice_tiles, slice_tiles));
+            classes.emplace_back(c + kItemOverheadTiles, per_slice);
+            items += per_slice;
+        }
+    }
+    if (items > kMaxSimulatedItems) return -1;
+    std::sort(classes.begin(), classes.end(), [](const auto& x, const auto& y) { return x.first > y.first; });
+    size_t m = 0;  // equal costs merged into one class
+    for (size_t i = 0; i < classes.size(); ++i) {
+        if (m > 0 && classes[m - 1].first == classes[i].first)
+            classes[m - 1].second += classes[i].second;
+        else
+            classes[m++] = classes[i];
+    }
+    classes.resize(m);
+    // a class of `count` equal workgroups: whole rounds of one per CU, then
+    // the rest on the least loaded CUs (list scheduling gives each of them to
+    // the CU that frees up first)
+    std::vector<int64_t> load(static_cast<size_t>(cus), 0);
+    int64_t base = 0;  // added to every CU
+    for (const auto& [cost, count] : classes) {
+        base += count / cus * cost;
+        const int64_t rest = count % cus;
+        if (rest == 0) continue;
+        std::nth_element(load.begin(), load.begin() + (rest - 1), load.end());
+        for (int64_t k = 0; k < rest; ++k) load[static_cast<size_t>(k)] += cost;
+    }
+    return base + *std::max_element(load.begin(), load.end());
+}
 
 // q_lens / k_rows: the launch's sequences (query rows, key rows)
 SplitPlan plan_split(const int32_t* q_lens, const int32_t* k_rows, int32_t n, int32_t heads, int32_t cus) {
@@ -90,17 +139,25 @@ SplitPlan plan_split(const int32_t* q_lens, const int32_t* k_rows, int32_t n, in
         work += static_cast<int64_t>((q_lens[i] + kQueryTile - 1) / kQueryTile) * kt * heads;
         longest = std::max(longest, kt);
     }
-    if (work <= 0) return {};
+    if (work <= 0 || cus < 1) return {};
     const double avg = static_cast<double>(work) / cus;
     if (longest <= 1.2 * avg) return {};
-    const int64_t s = std::min<int64_t>({kMaxSplits, static_cast<int64_t>(std::ceil(longest / avg)),
-                                         longest / kMinSplitTiles});
-    if (s < 2) return {};
-    SplitPlan sp;
-    const int32_t tiles = static_cast<int32_t>((longest + s - 1) / s);
-    sp.split_keys = tiles * kKeyTile;
-    sp.splits = (longest + tiles - 1) / tiles;  // no slice starts past the longest range
-    return sp.splits >= 2 ? sp : SplitPlan{};
+    SplitPlan best;
+    int64_t best_len = simulated_length(q_lens, k_rows, n, heads, cus, 1, 0);
+    if (best_len < 0) return {};
+    for (int32_t s = 2; s <= kMaxSplits && longest / s >= kMinSplitTiles; ++s) {
+        const int32_t tiles = (longest + s - 1) / s;
+        const int32_t slices = (longest + tiles - 1) / tiles;  // no slice starts past the longest range
+        if (slices != s) continue;  // the same split as a smaller s
+        const int64_t len = simulated_length(q_lens, k_rows, n, heads, cus, slices, tiles);
+        if (len < 0) break;
+        if (static_cast<double>(len) < kSplitGain * static_cast<double>(best_len)) {
+            best_len = len;
+            best.splits = slices;
+            best.split_keys = tiles * kKeyTile;
+        }
+    }
+    return best;
 }
 
 // Work queues of one persistent attention launch, as offsets (int32

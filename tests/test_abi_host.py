@@ -182,11 +182,33 @@ def test_prefill_scratch_size_and_param_checks():
         mla.mla_chunked_prefill_scratch_size(p)
 
 
+def _schedule_length(q_lens, k_rows, heads, cus, slices, slice_tiles):
+    """Tile steps of list scheduling the launch's workgroups on `cus` CUs,
+    longest first, each costing its key tiles (of its slice) plus one: the
+    workgroups of one cost go one per CU in whole rounds, the rest to the
+    least loaded CUs."""
+    count = {}
+    for q, k in zip(q_lens, k_rows):
+        if q <= 0:
+            continue
+        kt = (k + 63) // 64
+        for s in range(slices):
+            c = kt if slices == 1 else max(0, min(kt - s * slice_tiles, slice_tiles))
+            count[c + 1] = count.get(c + 1, 0) + (q + 255) // 256 * heads
+    loads = [0] * cus
+    for c in sorted(count, reverse=True):
+        rounds, rest = divmod(count[c], cus)
+        loads = sorted(x + rounds * c for x in loads)
+        loads = [x + c for x in loads[:rest]] + loads[rest:]
+    return max(loads)
+
+
 def _split_rule(q_lens, k_rows, heads, cus=256):
-    """Key slices of one chunk-attention launch, restated: split when the
+    """Key slices of one chunk-attention launch, restated: no split while the
     longest workgroup (one 256-query tile against a sequence's key tiles)
-    exceeds 1.2x the average CU load, into min(8, ceil(longest / average),
-    longest // 64) slices of equal whole tiles."""
+    stays within 1.2x the average CU load; otherwise the S in 2..16 (slices
+    of at least 64 whole tiles) whose list schedule is shortest, taken only
+    when 3% shorter than the best smaller S."""
     tiles = [(k + 63) // 64 for q, k in zip(q_lens, k_rows) if q > 0]
     work = sum((q + 255) // 256 * ((k + 63) // 64) * heads for q, k in zip(q_lens, k_rows) if q > 0)
     if not tiles or work == 0:
@@ -194,11 +216,17 @@ def _split_rule(q_lens, k_rows, heads, cus=256):
     longest, avg = max(tiles), work / cus
     if longest <= 1.2 * avg:
         return 1
-    s = min(8, math.ceil(longest / avg), longest // 64)
-    if s < 2:
-        return 1
-    per = -(-longest // s)
-    return -(-longest // per)
+    best, best_len = 1, _schedule_length(q_lens, k_rows, heads, cus, 1, 0)
+    for s in range(2, 17):
+        if longest // s < 64:
+            break
+        per = -(-longest // s)
+        if -(-longest // per) != s:
+            continue
+        n = _schedule_length(q_lens, k_rows, heads, cus, s, per)
+        if n < 0.97 * best_len:
+            best, best_len = s, n
+    return best
 
 
 def _scratch(ctx, q, heads, workspace_rows=32768):
@@ -222,6 +250,21 @@ def test_key_split_scratch_follows_the_split_rule(q, heads, ctx_split):
     up = lambda x: -(-x // 256) * 256  # noqa: E731
     expect = 0 if s == 1 else up(s * q * heads * 256) + up(s * heads * q * 4)
     assert diff == expect, (s, diff, expect)
+
+
+def test_key_split_balances_a_mixed_launch():
+    # one GPU's 16-head share of a chunk of the heterogeneous batch: two long
+    # requests and a short one.  Cutting at the average load (2 slices) leaves
+    # 384 equal workgroups for 256 CUs, two rounds on half of them; the list
+    # schedule picks 4 slices, which spread over the CUs in three even rounds
+    q, ctx, heads = [1905, 56, 1008], [67004, 414, 63616], 16
+    s = _split_rule(q, ctx, heads)
+    assert s == 4
+    assert _schedule_length(q, ctx, heads, 256, 4, 262) < 0.8 * _schedule_length(q, ctx, heads, 256, 2, 524)
+    up = lambda x: -(-x // 256) * 256  # noqa: E731
+    rows = sum(q)
+    diff = _scratch(ctx, q, heads, 200000) - _scratch([3000, 414, 3000], q, heads, 200000)
+    assert diff == up(s * rows * heads * 256) + up(s * heads * rows * 4)
 
 
 def test_kernel_kinds_match_header():

@@ -468,6 +468,8 @@ struct WindowProblem {
     int64_t e_req = 0, qsl = 0;
     std::vector<int64_t> it_start, it_off;
     std::vector<int32_t> it_rows;
+    std::vector<QueuePlan> it_queues;  // each iteration's attention launch
+    QueuePlan queues_suffix;
     std::vector<char> it_has_empty;
     int64_t tokens = 0;
     int32_t max_q = 0;
@@ -496,6 +498,8 @@ int build_window_problem(const mla_chunked_prefill_params& p, WindowProblem& pb)
 
     int64_t max_rows = 0;
     const int64_t w = pb.window;
+    const DeviceShape shape = device_shape();
+    std::vector<int32_t> lens(static_cast<size_t>(n));
     for (int32_t it = 0; it < pb.iterations; ++it) {
         pb.it_start.push_back(static_cast<int64_t>(pb.meta.size()));
         for (int32_t r = 0; r < n; ++r) pb.meta.push_back(static_cast<int32_t>(it * w));
@@ -507,12 +511,17 @@ int build_window_problem(const mla_chunked_prefill_params& p, WindowProblem& pb)
             const int64_t len = std::max<int64_t>(0, std::min<int64_t>(p.context_lens[r], (it + 1) * w) - it * w);
             empty = empty || len == 0;
             off += len;
+            lens[static_cast<size_t>(r)] = static_cast<int32_t>(len);
             pb.meta.push_back(static_cast<int32_t>(off));
         }
         pb.it_rows.push_back(static_cast<int32_t>(off));
         pb.it_has_empty.push_back(empty ? 1 : 0);
         max_rows = std::max(max_rows, off);
+        // the same persistent launches as the chunked path, so that the two
+        // schedulers differ only in their schedule
+        pb.it_queues.push_back(plan_queues(pb.meta, p.query_lens, lens.data(), n, p.num_heads, 1, false, shape.xcds));
     }
+    pb.queues_suffix = plan_queues(pb.meta, p.query_lens, nullptr, n, p.num_heads, 1, true, shape.xcds);
 
     const int64_t H = p.num_heads, T = pb.tokens;
     Layout& L = pb.lay;
@@ -807,6 +816,20 @@ int mla_uniform_window_prefill(const mla_chunked_prefill_params* params, void* s
     MLA_TRY(upload(pb.meta.data(), pb.meta.size() * sizeof(int32_t), meta, stream));
     const bf16_t* q = static_cast<const bf16_t*>(p.q);
     const int32_t* qsl = meta + pb.qsl;
+    // attention over all N requests, through the launch's work queues when it has them
+    auto window_attention = [&](const bf16_t* qa, const bf16_t* ka, const bf16_t* va, const int32_t* cu_q,
+                                const int32_t* cu_k, bool causal, bf16_t* dst, float* dst_lse,
+                                const QueuePlan& qp) -> int {
+        if (qp.table < 0)
+            return launch_attention(qa, ka, va, cu_q, cu_k, N, pb.max_q, H, p.scale, causal, dst, dst_lse, T, stream);
+        WorkQueues wq;
+        wq.table = meta + qp.table;
+        wq.counters = meta + qp.counters;
+        wq.num_seqs = qp.n;
+        wq.queues = qp.queues;
+        wq.items = qp.items;
+        return launch_attention_persistent(qa, ka, va, cu_q, cu_k, N, H, p.scale, causal, dst, dst_lse, T, wq, stream);
+    };
 
     for (int32_t it = 0; it < pb.iterations; ++it) {
         const int32_t* e_off = meta + pb.it_off[it];
@@ -816,14 +839,14 @@ int mla_uniform_window_prefill(const mla_chunked_prefill_params* params, void* s
         // iteration 0 is the context state itself; later ones go through the temporary
         bf16_t* o = it == 0 ? part_out : tmp_out;
         float* l = it == 0 ? part_lse : tmp_lse;
-        MLA_TRY(launch_attention(q, ws_k, ws_v, qsl, e_off, N, pb.max_q, H, p.scale, false, o, l, T, stream));
+        MLA_TRY(window_attention(q, ws_k, ws_v, qsl, e_off, false, o, l, pb.it_queues[it]));
         if (pb.it_has_empty[it]) MLA_TRY(launch_mask_empty_context(l, T, o, 2, qsl, e_off, N, T, H, kDv, stream));
         if (it > 0) MLA_TRY(launch_merge(part_out, part_lse, part_out, part_lse, tmp_out, tmp_lse, T, H, kDv, T, T, T,
                                          T, stream));
     }
 
-    MLA_TRY(launch_attention(q, static_cast<const bf16_t*>(p.k_new), static_cast<const bf16_t*>(p.v_new), qsl, qsl,
-                             N, pb.max_q, H, p.scale, true, suf_out, suf_lse, T, stream));
+    MLA_TRY(window_attention(q, static_cast<const bf16_t*>(p.k_new), static_cast<const bf16_t*>(p.v_new), qsl, qsl,
+                             true, suf_out, suf_lse, pb.queues_suffix));
     MLA_TRY(launch_merge(static_cast<bf16_t*>(p.out), p.out_lse, part_out, part_lse, suf_out, suf_lse, T, H, kDv,
                          T, T, T, pb.prefix_num_tokens, stream));
     return MLA_OK;

@@ -58,11 +58,14 @@ def test_named_small_workloads_full(idx):
 # Chunk-attention launches whose longest workgroup outlasts the average CU load
 # (work = heads x sum of query tiles x key tiles, over 256 CUs) cut each
 # sequence's key range into slices and LSE-merge the slice states.  Each case's
-# split count follows from min(8, ceil(longest / average), longest // 64) key
-# tiles and is given in the comment.
+# split count is the one with the shortest longest-first list schedule over
+# the CUs (slices of at least 64 key tiles, at most 16; restated in
+# tests/test_abi_host.py) and is given in the comment.
 SPLIT_CASES = [
     # one chunk, 4 workgroups of 469 key tiles: 7 slices in one merge
     W.Workload("split_single", (30000,), (20,), 4, 32768, 64, 64, 1.0, 501),
+    # 2 workgroups of 1024 key tiles: 16 slices, the most one merge combines
+    W.Workload("split_sixteen", (65536,), (3,), 2, 65536, 64, 64, 1.0, 506),
     # chunk 0: request 0's first 16384 rows, 4 slices; chunk 1: its continuation
     # (13616 rows) in a launch of its own, 3 slices, then request 1's head
     W.Workload("split_continuation", (30000, 9000, 0), (5, 3, 2), 2, 16384, 64, 64, 1.0, 502),

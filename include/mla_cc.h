@@ -27,8 +27,8 @@
  *     r is in block block_table[r * block_table_width + p / block_size], slot
  *     p % block_size.
  *   - `stream` is a hipStream_t (NULL = the default stream).  Device calls only
- *     enqueue work on it and allocate no device memory.  The one host wait is
- *     in the metadata upload of mla_chunked_prefill, mla_dcp_chunked_prefill
+ *     enqueue work on it and allocate no device memory.  The only host waits
+ *     are in the metadata upload of mla_chunked_prefill, mla_dcp_chunked_prefill
  *     and mla_uniform_window_prefill (see mla_chunked_prefill).
  *   - An empty attention state is LSE = -inf with output 0.  Merges select
  *     rather than multiply by zero, so the output of an empty side is never
@@ -318,10 +318,12 @@ int mla_chunked_prefill_scratch_size(const mla_chunked_prefill_params* params, i
  * workgroup (one 256-query tile of one head against a request's rows) would
  * outlast the average load of the device's CUs (256 on MI355X) is cut along
  * the key axis:
- * each request's rows are split into 2..8 slices of at least 4096 rows, one
- * state per slice goes to the scratch, and one merge combines the slices into
- * the destination rows in fp32 (exact up to rounding: the LSE combination of
- * disjoint key sets, as merge_attn_states forms it for two).  The attention
+ * each request's rows are split into 2..16 slices of at least 4096 rows (the
+ * count whose longest-first schedule over the CUs, simulated on the host, is
+ * shortest), one state per slice goes to the scratch, and one merge combines
+ * the slices into the destination rows in fp32 (exact up to rounding: the LSE
+ * combination of disjoint key sets, as merge_attn_states forms it for two).
+ * The attention
  * launches are persistent: one workgroup per CU takes (sequence, head, query
  * tile) items from per-XCD queues, longest sequences first (causal: tile
  * Q-1-i paired with tile i), and moves on to the other XCDs' queues when its
@@ -386,8 +388,11 @@ int mla_uniform_window_prefill_scratch_size(const mla_chunked_prefill_params* pa
  * context state with it over all tokens.  Then the causal suffix attention
  * and the final merge with prefix_num_tokens, as in mla_chunked_prefill.
  * Same params and conventions as mla_chunked_prefill (max_context_chunk is
- * not used; split_alignment rounds the window).  Kept to measure the
- * scheduler change; it computes the same result up to rounding.
+ * not used; split_alignment rounds the window).  Its attention launches are
+ * the same persistent launches as mla_chunked_prefill's (work queues per
+ * iteration and for the suffix, in the uploaded metadata), without key
+ * splits.  Kept to measure the scheduler change; it computes the same result
+ * up to rounding.
  */
 int mla_uniform_window_prefill(const mla_chunked_prefill_params* params, void* stream);
 

@@ -439,14 +439,15 @@ __device__ __forceinline__ void attention_tile(const AttnArgs& a, int32_t seq, i
 
         // ---- mask keys of S(j) past the end (and above the diagonal when causal)
         if (active && ((k0 + kBlockN > kv_end) || (kDiag && k0 + kBlockN - 1 > wave_first_q))) {
+            // element (kb, r) holds key k0 + g*4 + kb*32 + (r>>2)*8 + (r&3); the
+            // lane's live keys end at min(kv_end - 1, its query row): one
+            // compare of a constant against that limit per element
+            const int32_t lim = (kDiag ? min(kv_end - 1, q_row) : kv_end - 1) - k0 - g * 4;
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int32_t key = k0 + kb * 32 + (r >> 2) * 8 + g * 4 + (r & 3);
-                    const bool dead = key >= kv_end || (kDiag && key > q_row);
-                    if (dead) s_cur[kb][r] = -INFINITY;
-                }
+                for (int r = 0; r < 16; ++r)
+                    if (kb * 32 + (r >> 2) * 8 + (r & 3) > lim) s_cur[kb][r] = -INFINITY;
         }
 
         auto scores_next = [&]() {

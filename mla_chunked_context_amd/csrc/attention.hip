@@ -711,8 +711,7 @@ __global__ __launch_bounds__(kThreads, 1) void suffix_attention_queued_kernel(At
     __shared__ __attribute__((aligned(16))) bf16_t vt_lds[2 * kVtTileElems];
     __shared__ int32_t table[kMaxQueueTableInts];
     __shared__ int32_t s_next[5];
-    __shared__ __attribute__((aligned(256))) unsigned char dump[kPrefetchDumpBytes];
-    attention_queues<true>(a, w, k_lds, vt_lds, table, s_next, dump);
+    attention_queues<true>(a, w, k_lds, vt_lds, table, s_next, nullptr);  // no next-tile prefetch
 }
 
 }  // namespace

@@ -53,6 +53,10 @@ enum {
 
 #define MLA_QK_HEAD_DIM 192
 #define MLA_V_HEAD_DIM 128
+/* Most heads the attention entry points and the prefill drivers accept (the
+ * kernels address one key tile of all heads with 32-bit byte offsets).  More
+ * gives MLA_ERR_INVALID_ARG. */
+#define MLA_MAX_HEADS 1024
 #define MLA_ABI_VERSION 1
 /* Size of the library's own device scratch used by mla_chunked_prefill_no_alloc (128 MiB per device). */
 #define MLA_NO_ALLOC_SCRATCH_BYTES (128ull << 20)
@@ -214,7 +218,7 @@ int mla_dcp_reorganize_context(const void* gathered_k, const void* gathered_v, i
  *   max_q       >= every cu_q[i+1] - cu_q[i] (rows past it are not computed)
  *   out  dev bf16 [Tq, H, 128]    lse dev fp32 [H, lse_head_stride >= Tq]
  * A sequence with no keys gets (0, -inf).  Only rows of the listed sequences
- * are written.
+ * are written.  1 <= num_heads <= MLA_MAX_HEADS.
  */
 int mla_context_chunk_attn(const void* q, const void* k, const void* v, const int32_t* cu_q,
                            const int32_t* cu_k, int32_t num_seqs, int32_t max_q, int32_t num_heads,
@@ -290,7 +294,7 @@ typedef struct mla_chunked_prefill_params {
     const int32_t* context_lens; /* host int32 [num_requests] */
     const int32_t* query_lens;   /* host int32 [num_requests] */
     int32_t num_requests;
-    int32_t num_heads;
+    int32_t num_heads;         /* 1 .. MLA_MAX_HEADS */
     float scale;
     int64_t workspace_rows;    /* row_budget of the planner */
     int64_t max_context_chunk; /* <= 0: workspace_rows */

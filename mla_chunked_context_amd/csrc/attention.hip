@@ -169,8 +169,8 @@ struct NoHook {
 
 // The tile a workgroup takes next, known before its current tile ends: the
 // pair's second tile, or the next item (decoded into LDS during the current
-// item's prologue).  Its first loads are fetched into L2 during the current
-// tile's second-to-last step, so that its prologue reads L2, not HBM.
+// item's prologue).  Its first loads are fetched into L2 a few steps before
+// the current tile ends, so that its prologue reads L2, not HBM.
 struct NextTile {
     const int32_t* item;  // LDS: seq, head, split, qt of the next item (seq < 0: none), or null
     int32_t qt2;          // >= 0: the pair's second tile (same sequence, head and split, reversed)
@@ -797,7 +797,7 @@ namespace {
 int check_attention_args(const void* q, const void* k, const void* v, const int32_t* cu_q, int32_t num_seqs,
                          int32_t max_q, int32_t num_heads, float scale, const void* out, const float* lse,
                          int64_t lse_head_stride) {
-    if (num_seqs < 0 || max_q < 0 || num_heads < 1) return MLA_ERR_INVALID_ARG;
+    if (num_seqs < 0 || max_q < 0 || num_heads < 1 || num_heads > MLA_MAX_HEADS) return MLA_ERR_INVALID_ARG;
     if (!(scale > 0.f) || !std::isfinite(scale)) return MLA_ERR_INVALID_ARG;
     if (num_seqs == 0 || max_q == 0) return MLA_OK;
     if (q == nullptr || k == nullptr || v == nullptr || cu_q == nullptr || out == nullptr || lse == nullptr)

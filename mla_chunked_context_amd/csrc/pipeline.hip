@@ -392,7 +392,8 @@ int upload(const void* src, size_t bytes, void* dst, hipStream_t stream) {
 
 int check_params(const mla_chunked_prefill_params* p) {
     if (p == nullptr) return MLA_ERR_INVALID_ARG;
-    if (p->num_requests < 0 || p->num_heads < 1 || p->block_size < 1 || p->block_table_width < 0 ||
+    if (p->num_requests < 0 || p->num_heads < 1 || p->num_heads > MLA_MAX_HEADS || p->block_size < 1 ||
+        p->block_table_width < 0 ||
         p->num_blocks < 0 || p->workspace_rows < 1 || p->split_alignment < 1)
         return MLA_ERR_INVALID_ARG;
     if (!(p->scale > 0.f) || !std::isfinite(p->scale)) return MLA_ERR_INVALID_ARG;

@@ -161,6 +161,23 @@ def test_device_calls_reject_bad_arguments_without_gpu():
                                    ctypes.c_int64(0), ctypes.c_int64(0), ctypes.c_int64(0), None) == 0
 
 
+def test_head_count_bound():
+    # the attention kernels address a key tile of all heads with 32-bit byte
+    # offsets; head counts past MLA_MAX_HEADS are refused before any HIP call
+    f = mla._lib
+    args = lambda h: (ctypes.c_void_p(256), ctypes.c_void_p(256), ctypes.c_void_p(256), ctypes.c_void_p(256),  # noqa: E731
+                      ctypes.c_void_p(256), 1, 4, h, ctypes.c_float(0.07), ctypes.c_void_p(256),
+                      ctypes.c_void_p(256), ctypes.c_int64(4), None)
+    assert f.mla_context_chunk_attn(*args(1025)) == mla.MLA_ERR_INVALID_ARG
+    wl = W.named_workloads()[1]
+    q = torch.empty((wl.num_tokens, 1025, W.DK), dtype=torch.bfloat16, device="meta")
+    p = mla.make_prefill_params(q, q, q, None, None, None, wl.context_lens, wl.query_lens, wl.workspace_rows,
+                                wl.split_alignment, wl.scale)
+    with pytest.raises(mla.MlaError) as e:
+        mla.mla_chunked_prefill_scratch_size(p)
+    assert e.value.status == mla.MLA_ERR_INVALID_ARG
+
+
 def test_prefill_scratch_size_and_param_checks():
     wl = W.named_workloads()[5]
     p = mla.ChunkedPrefillParams()

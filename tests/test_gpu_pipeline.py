@@ -153,6 +153,20 @@ def test_run_twice_is_bitwise_identical():
     assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)) and torch.equal(l1, l2)
 
 
+@pytest.mark.parametrize("name", ["split_continuation", "split_sixteen", "split_ragged"])
+def test_queued_and_split_launches_are_repeatable(name):
+    # which CU takes which item of a persistent launch changes from run to run
+    # (per-XCD queues, stealing); each item's arithmetic and each merge's order
+    # do not, so repeated runs agree bit for bit
+    wl = [w for w in SPLIT_CASES if w.name == name][0]
+    say(f"repeatability {name}")
+    b = W.make_batch(wl, device=DEV, gen_device="cpu")
+    o1, l1 = run_prefill(mla, b)
+    for _ in range(3):
+        o2, l2 = run_prefill(mla, b)
+        assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)) and torch.equal(l1, l2)
+
+
 # ------------------------------------------------------------- full sizes
 
 

@@ -71,6 +71,12 @@ constexpr int kKLoads = kBlockN * kKVecPerRow / kThreads;  // 3 direct-to-LDS lo
 constexpr int kVLoads = 2;                                  // 2 keys x 8 dims per thread
 constexpr int kKTileBytes = kBlockN * kKRowBytes;  // 24 KB
 constexpr int kVtTileElems = kDv * kVtStride;
+// Causal kernels: Q rows of a tile reach LDS with direct-to-LDS loads over
+// whole cache lines (like K) before they are read as MFMA fragments; the
+// staging area holds the tile's 256 rows and doubles as the V^T ring.
+constexpr int kQStageBytes = kBlockM * kKRowBytes;  // 96 KB
+constexpr int kQStageWaveBytes = kQPerWave * kKRowBytes;  // 12 KB
+static_assert(kQStageBytes >= 2 * kVtTileElems * 2, "the V^T ring lies inside the Q staging area");
 constexpr float kRescaleThreshold = 8.0f;  // log2 units
 constexpr int kBufferConfig = 0x00020000;  // dword 3 of a raw buffer descriptor on gfx9
 // s_waitcnt immediate on gfx9: vmcnt in bits 3:0 (and 15:14), expcnt 6:4, lgkmcnt 11:8;
@@ -237,7 +243,8 @@ __device__ __forceinline__ void prefetch_tile(const AttnArgs& a, int32_t seq, in
 template <bool kCausal, class Hook>
 __device__ __forceinline__ void attention_tile(const AttnArgs& a, int32_t seq, int32_t head, int32_t split,
                                                int32_t qt, bool reverse, unsigned char* k_lds, bf16_t* vt_lds,
-                                               Hook& hook, const NextTile& next, unsigned char* dump) {
+                                               Hook& hook, const NextTile& next, unsigned char* dump,
+                                               unsigned char* q_stage) {
     hook.begin();
     const int32_t q_begin = a.cu_q[seq];
     const int32_t q_len = a.cu_q[seq + 1] - q_begin;
@@ -261,11 +268,36 @@ __device__ __forceinline__ void attention_tile(const AttnArgs& a, int32_t seq, i
     const int g = lane >> 5;
     const int H = a.heads;
 
-    // ---- Q fragments (B operand of S^T = K Q^T), kept in registers
+    // ---- Q fragments (B operand of S^T = K Q^T), kept in registers.  Every
+    // fragment load serves 32 rows (a lane reads its own query's row), so it
+    // touches 32 cache lines for 1 KB: loaded so, a tile's Q costs the memory
+    // pipeline about as much as all its other first loads together.  With
+    // q_stage, each wave instead copies its 32 rows (12 KB) into LDS with
+    // direct-to-LDS loads of 1 KB each (about 9 lines), in the K tile's
+    // swizzled row layout, and reads the fragments from there once they land.
     const int32_t q_row = qt * kBlockM + wave * kQPerWave + l32;  // row inside the sequence
     const bool q_valid = q_row < q_len;
     bf16x8 qf[kDk / 16];
-    {
+    if (q_stage != nullptr) {
+        const int32_t rows = max(0, min(kQPerWave, q_len - (q_row - l32)));  // rows past the end read as zero
+        const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<bf16_t*>(a.q + (static_cast<int64_t>(q_begin + q_row - l32) * H + head) * kDk), 0,
+            rows * H * kDk * 2, kBufferConfig);
+        unsigned char* dst = q_stage + wave * kQStageWaveBytes;
+        // the lane-only offsets are computed here for every tile rather than
+        // once per launch (they would be held in registers through the key loop)
+        int lane_t = lane;
+        asm volatile("" : "+v"(lane_t));
+#pragma unroll
+        for (int i = 0; i < kQStageWaveBytes / 1024; ++i) {
+            // lane writes 16 bytes at i * 1024 + lane * 16: row r, position c ^ ((r >> 1) & 7) holds chunk c
+            const int p = i * 64 + lane_t;
+            const int r = p / kKVecPerRow;
+            const int c = (p % kKVecPerRow) ^ ((r >> 1) & 7);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, (__attribute__((address_space(3))) void*)(dst + i * 1024),
+                                                     16, r * H * kDk * 2 + c * 16, 0, 0, 0);
+        }
+    } else {
         const uint4* qp = reinterpret_cast<const uint4*>(
             a.q + (static_cast<int64_t>(q_begin + (q_valid ? q_row : 0)) * H + head) * kDk + g * 8);
 #pragma unroll
@@ -398,7 +430,8 @@ __device__ __forceinline__ void attention_tile(const AttnArgs& a, int32_t seq, i
     // The barrier at the end of the iteration publishes them.
     // Prologue: one round trip.  Q, K(0), K(1) (straight into LDS), V(0) and
     // V(1) (registers) are all in flight together; V(0) is stored once they
-    // have landed, V(1) at the start of iteration 0.
+    // have landed (and, with staged Q, once every wave has read its Q rows out
+    // of the area the V^T ring shares), V(1) at the start of iteration 0.
     f32x16 s_cur[2], s_nxt[2];
     if (n_tiles > 0) {
         load_k(key0(0), 0);
@@ -412,10 +445,19 @@ __device__ __forceinline__ void attention_tile(const AttnArgs& a, int32_t seq, i
     // prologue's conditional QK leaves a path where they are not, and the loop
     // would otherwise wait for all loads before its first QK MFMA)
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    if (q_stage != nullptr) {
+        // the same per-lane addresses as the K fragments (row l32 of the wave's
+        // rows, the same swizzle), moved to the wave's staging rows
+        const int32_t qs = static_cast<int32_t>(q_stage - k_lds) + wave * kQStageWaveBytes;
+#pragma unroll
+        for (int ks = 0; ks < kDk / 16; ++ks)
+            qf[ks] = *reinterpret_cast<const bf16x8*>(k_lane[ks & 3] + qs + (ks >> 2) * 128);
+        __syncthreads();  // every wave's rows are read (and every K DMA has landed)
+    }
     if (n_tiles > 0) store_v(0);
 #pragma unroll
     for (int u = 0; u < kVLoads; ++u) vreg[u] = vreg1[u];
-    __syncthreads();
+    if (q_stage == nullptr) __syncthreads();
     hook.after_prologue();
     if (n_tiles > 0 && (!kCausal || key0(0) <= wave_last_q)) qk(s_cur, std::integral_constant<int, 0>{});
     __syncthreads();  // K(0) is overwritten by K(2) at the end of iteration 0
@@ -563,19 +605,37 @@ __device__ __forceinline__ void attention_tile(const AttnArgs& a, int32_t seq, i
         run(n_tiles, std::false_type{});
     }
 
-    // ---- epilogue: normalise, write bf16 output rows and the LSE
+    // ---- epilogue: normalise, write bf16 output rows and the LSE.
+    // Every store instruction writes 32 rows (one per query of the wave), so
+    // it costs the memory pipeline about one cycle per row whatever its width:
+    // the rows are written 16 bytes per lane (eight instructions), not in the
+    // accumulator's 8-byte pieces (sixteen).  A tile's stores are still in the
+    // pipeline when the next tile's first loads are issued.
     const float l_tot = pair_sum(l_run);
     if (!q_valid) return;
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    bf16_t* orow = out + (static_cast<int64_t>(q_begin + q_row) * H + head) * kDv + g * 4;
+    {
+        // lane (l32, g) holds dims c*8 + g*4 .. +3 of every 8-dim chunk c of
+        // its query; one swap across the lane pair per dword gives the lower
+        // lane all of chunk 2m and the upper lane all of chunk 2m+1, written
+        // as one 16-byte store each.
+        bf16_t* orow = out + (static_cast<int64_t>(q_begin + q_row) * H + head) * kDv + g * 8;
 #pragma unroll
-    for (int db = 0; db < kDv / 32; ++db)
+        for (int db = 0; db < kDv / 32; ++db)
 #pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-            const uint32_t lo = pack_bf16x2(o_acc[db][r4 * 4 + 0] * inv, o_acc[db][r4 * 4 + 1] * inv);
-            const uint32_t hi = pack_bf16x2(o_acc[db][r4 * 4 + 2] * inv, o_acc[db][r4 * 4 + 3] * inv);
-            *reinterpret_cast<uint2*>(orow + db * 32 + r4 * 8) = make_uint2(lo, hi);
-        }
+            for (int m = 0; m < 2; ++m) {
+                const int r0 = 2 * m * 4, r1 = (2 * m + 1) * 4;  // accumulator slots of chunks 2m, 2m+1
+                const uint32_t p0 = pack_bf16x2(o_acc[db][r0 + 0] * inv, o_acc[db][r0 + 1] * inv);
+                const uint32_t p1 = pack_bf16x2(o_acc[db][r0 + 2] * inv, o_acc[db][r0 + 3] * inv);
+                const uint32_t q0 = pack_bf16x2(o_acc[db][r1 + 0] * inv, o_acc[db][r1 + 1] * inv);
+                const uint32_t q1 = pack_bf16x2(o_acc[db][r1 + 2] * inv, o_acc[db][r1 + 3] * inv);
+                const auto s0 = __builtin_amdgcn_permlane32_swap(p0, q0, false, false);
+                const auto s1 = __builtin_amdgcn_permlane32_swap(p1, q1, false, false);
+                // lower lanes: (own P, upper's P) = (p, s[1]); upper lanes: (lower's Q, own Q) = (s[0], q)
+                const uint4 x = g == 0 ? make_uint4(p0, p1, s0[1], s1[1]) : make_uint4(s0[0], s1[0], q0, q1);
+                *reinterpret_cast<uint4*>(orow + db * 32 + m * 16) = x;
+            }
+    }
     if (g == 0) {
         const float lse = l_tot > 0.f ? (m_run + log2f(l_tot)) * 0.69314718055994531f : -INFINITY;
         lse_out[head * a.lse_stride + q_begin + q_row] = lse;
@@ -584,7 +644,8 @@ __device__ __forceinline__ void attention_tile(const AttnArgs& a, int32_t seq, i
 
 // Grid form: workgroup bid computes one logical tile.
 template <bool kCausal>
-__device__ __forceinline__ void attention_grid(const AttnArgs& a, unsigned char* k_lds, bf16_t* vt_lds) {
+__device__ __forceinline__ void attention_grid(const AttnArgs& a, unsigned char* k_lds, bf16_t* vt_lds,
+                                               unsigned char* q_stage) {
     const int32_t tile = xcd_logical_tile(blockIdx.x, a.total_tiles, a.q_tiles, a.num_xcd);
     int32_t qt = tile % a.q_tiles;
     int32_t rest = tile / a.q_tiles;
@@ -595,7 +656,8 @@ __device__ __forceinline__ void attention_grid(const AttnArgs& a, unsigned char*
     if (kCausal) qt = a.q_tiles - 1 - qt;  // longest causal tiles first
     if (qt * kBlockM >= a.cu_q[seq + 1] - a.cu_q[seq]) return;
     NoHook hook;
-    attention_tile<kCausal>(a, seq, head, split, qt, false, k_lds, vt_lds, hook, NextTile{nullptr, -1}, nullptr);
+    attention_tile<kCausal>(a, seq, head, split, qt, false, k_lds, vt_lds, hook, NextTile{nullptr, -1}, nullptr,
+                            q_stage);
 }
 
 // Persistent form.  Thread 0 takes items: one atomic increment of its
@@ -650,7 +712,7 @@ struct QueueHook {
 template <bool kCausal>
 __device__ __forceinline__ void attention_queues(const AttnArgs& a, const QueueArgs& w, unsigned char* k_lds,
                                                  bf16_t* vt_lds, int32_t* table, int32_t* s_next,
-                                                 unsigned char* dump) {
+                                                 unsigned char* dump, unsigned char* q_stage) {
     for (int32_t i = threadIdx.x; i < w.table_ints; i += kThreads) table[i] = w.table[i];
     QueueHook hook;
     hook.w = &w;
@@ -679,7 +741,8 @@ __device__ __forceinline__ void attention_queues(const AttnArgs& a, const QueueA
         for (int32_t t = 0; t < n_items; ++t) {
             hook.enabled = t == 0;
             const NextTile next{s_next, t + 1 < n_items ? qt2 : -1};
-            attention_tile<kCausal>(a, seq, head, split, t == 0 ? qt : qt2, t == 1, k_lds, vt_lds, hook, next, dump);
+            attention_tile<kCausal>(a, seq, head, split, t == 0 ? qt : qt2, t == 1, k_lds, vt_lds, hook, next, dump,
+                                    q_stage);
         }
     }
 }
@@ -688,13 +751,13 @@ __device__ __forceinline__ void attention_queues(const AttnArgs& a, const QueueA
 __global__ __launch_bounds__(kThreads, 1) void chunk_attention_kernel(AttnArgs a) {
     __shared__ __attribute__((aligned(1024))) unsigned char k_lds[2 * kKTileBytes];
     __shared__ __attribute__((aligned(16))) bf16_t vt_lds[2 * kVtTileElems];
-    attention_grid<false>(a, k_lds, vt_lds);
+    attention_grid<false>(a, k_lds, vt_lds, nullptr);
 }
 
 __global__ __launch_bounds__(kThreads, 1) void suffix_attention_kernel(AttnArgs a) {
     __shared__ __attribute__((aligned(1024))) unsigned char k_lds[2 * kKTileBytes];
-    __shared__ __attribute__((aligned(16))) bf16_t vt_lds[2 * kVtTileElems];
-    attention_grid<true>(a, k_lds, vt_lds);
+    __shared__ __attribute__((aligned(1024))) unsigned char vq_lds[kQStageBytes];  // V^T ring and Q staging
+    attention_grid<true>(a, k_lds, reinterpret_cast<bf16_t*>(vq_lds), vq_lds);
 }
 
 __global__ __launch_bounds__(kThreads, 1) void chunk_attention_queued_kernel(AttnArgs a, QueueArgs w) {
@@ -703,15 +766,16 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_attention_queued_kernel(Att
     __shared__ int32_t table[kMaxQueueTableInts];
     __shared__ int32_t s_next[5];
     __shared__ __attribute__((aligned(256))) unsigned char dump[kPrefetchDumpBytes];
-    attention_queues<false>(a, w, k_lds, vt_lds, table, s_next, dump);
+    attention_queues<false>(a, w, k_lds, vt_lds, table, s_next, dump, nullptr);
 }
 
 __global__ __launch_bounds__(kThreads, 1) void suffix_attention_queued_kernel(AttnArgs a, QueueArgs w) {
     __shared__ __attribute__((aligned(1024))) unsigned char k_lds[2 * kKTileBytes];
-    __shared__ __attribute__((aligned(16))) bf16_t vt_lds[2 * kVtTileElems];
+    __shared__ __attribute__((aligned(1024))) unsigned char vq_lds[kQStageBytes];  // V^T ring and Q staging
     __shared__ int32_t table[kMaxQueueTableInts];
     __shared__ int32_t s_next[5];
-    attention_queues<true>(a, w, k_lds, vt_lds, table, s_next, nullptr);  // no next-tile prefetch
+    // no next-tile prefetch
+    attention_queues<true>(a, w, k_lds, reinterpret_cast<bf16_t*>(vq_lds), table, s_next, nullptr, vq_lds);
 }
 
 }  // namespace

@@ -25,7 +25,9 @@ constexpr int32_t kQueryTileRows = 256;  // queries per attention tile
 // pair of query tiles, the longest left with the shortest left (tiles Q-1-i
 // and i of Q): every pair but a lone middle tile then costs Q + 1 key blocks.
 constexpr int32_t kCounterStride = 16;       // ints between two queues' counters (64 bytes)
-constexpr int32_t kMaxQueueTableInts = 4096; // table held in LDS by the kernel
+// table held in LDS by the kernel (the causal kernel's LDS holds it beside
+// 144 KB of K ring and Q staging)
+constexpr int32_t kMaxQueueTableInts = 4080;
 
 struct WorkQueues {
     const int32_t* table = nullptr;  // work_table_ints(...) ints

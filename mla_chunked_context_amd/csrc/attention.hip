@@ -762,11 +762,14 @@ __global__ __launch_bounds__(kThreads, 1) void suffix_attention_kernel(AttnArgs 
 
 __global__ __launch_bounds__(kThreads, 1) void chunk_attention_queued_kernel(AttnArgs a, QueueArgs w) {
     __shared__ __attribute__((aligned(1024))) unsigned char k_lds[2 * kKTileBytes];
-    __shared__ __attribute__((aligned(16))) bf16_t vt_lds[2 * kVtTileElems];
+    // V^T ring and Q staging; the next-tile prefetch lands past the V^T ring
+    // (those loads complete within the step that issues them, before any
+    // later tile stages its Q there)
+    __shared__ __attribute__((aligned(1024))) unsigned char vq_lds[kQStageBytes];
     __shared__ int32_t table[kMaxQueueTableInts];
     __shared__ int32_t s_next[5];
-    __shared__ __attribute__((aligned(256))) unsigned char dump[kPrefetchDumpBytes];
-    attention_queues<false>(a, w, k_lds, vt_lds, table, s_next, dump, nullptr);
+    attention_queues<false>(a, w, k_lds, reinterpret_cast<bf16_t*>(vq_lds), table, s_next,
+                            vq_lds + kQStageBytes - kPrefetchDumpBytes, vq_lds);
 }
 
 __global__ __launch_bounds__(kThreads, 1) void suffix_attention_queued_kernel(AttnArgs a, QueueArgs w) {

@@ -71,9 +71,9 @@ constexpr int kKLoads = kBlockN * kKVecPerRow / kThreads;  // 3 direct-to-LDS lo
 constexpr int kVLoads = 2;                                  // 2 keys x 8 dims per thread
 constexpr int kKTileBytes = kBlockN * kKRowBytes;  // 24 KB
 constexpr int kVtTileElems = kDv * kVtStride;
-// Causal kernels: Q rows of a tile reach LDS with direct-to-LDS loads over
-// whole cache lines (like K) before they are read as MFMA fragments; the
-// staging area holds the tile's 256 rows and doubles as the V^T ring.
+// Q rows of a tile reach LDS with direct-to-LDS loads over whole cache lines
+// (like K) before they are read as MFMA fragments; the staging area holds the
+// tile's 256 rows and doubles as the V^T ring.
 constexpr int kQStageBytes = kBlockM * kKRowBytes;  // 96 KB
 constexpr int kQStageWaveBytes = kQPerWave * kKRowBytes;  // 12 KB
 static_assert(kQStageBytes >= 2 * kVtTileElems * 2, "the V^T ring lies inside the Q staging area");
@@ -268,17 +268,18 @@ __device__ __forceinline__ void attention_tile(const AttnArgs& a, int32_t seq, i
     const int g = lane >> 5;
     const int H = a.heads;
 
-    // ---- Q fragments (B operand of S^T = K Q^T), kept in registers.  Every
-    // fragment load serves 32 rows (a lane reads its own query's row), so it
-    // touches 32 cache lines for 1 KB: loaded so, a tile's Q costs the memory
-    // pipeline about as much as all its other first loads together.  With
-    // q_stage, each wave instead copies its 32 rows (12 KB) into LDS with
-    // direct-to-LDS loads of 1 KB each (about 9 lines), in the K tile's
-    // swizzled row layout, and reads the fragments from there once they land.
+    // ---- Q fragments (B operand of S^T = K Q^T), kept in registers.  A
+    // fragment load straight from global memory would serve 32 rows (a lane
+    // reads its own query's row) and touch 32 cache lines for 1 KB: a tile's Q
+    // would then cost the memory pipeline about as much as all its other first
+    // loads together.  Each wave instead copies its 32 rows (12 KB) into its
+    // part of q_stage with direct-to-LDS loads of 1 KB each (about 9 lines), in
+    // the K tile's swizzled row layout, and reads the fragments from there once
+    // they land.
     const int32_t q_row = qt * kBlockM + wave * kQPerWave + l32;  // row inside the sequence
     const bool q_valid = q_row < q_len;
     bf16x8 qf[kDk / 16];
-    if (q_stage != nullptr) {
+    {
         const int32_t rows = max(0, min(kQPerWave, q_len - (q_row - l32)));  // rows past the end read as zero
         const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
             const_cast<bf16_t*>(a.q + (static_cast<int64_t>(q_begin + q_row - l32) * H + head) * kDk), 0,
@@ -296,15 +297,6 @@ __device__ __forceinline__ void attention_tile(const AttnArgs& a, int32_t seq, i
             const int c = (p % kKVecPerRow) ^ ((r >> 1) & 7);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, (__attribute__((address_space(3))) void*)(dst + i * 1024),
                                                      16, r * H * kDk * 2 + c * 16, 0, 0, 0);
-        }
-    } else {
-        const uint4* qp = reinterpret_cast<const uint4*>(
-            a.q + (static_cast<int64_t>(q_begin + (q_valid ? q_row : 0)) * H + head) * kDk + g * 8);
-#pragma unroll
-        for (int ks = 0; ks < kDk / 16; ++ks) {
-            uint4 x = make_uint4(0u, 0u, 0u, 0u);
-            if (q_valid) x = qp[ks * 2];
-            qf[ks] = __builtin_bit_cast(bf16x8, x);
         }
     }
 
@@ -430,8 +422,8 @@ __device__ __forceinline__ void attention_tile(const AttnArgs& a, int32_t seq, i
     // The barrier at the end of the iteration publishes them.
     // Prologue: one round trip.  Q, K(0), K(1) (straight into LDS), V(0) and
     // V(1) (registers) are all in flight together; V(0) is stored once they
-    // have landed (and, with staged Q, once every wave has read its Q rows out
-    // of the area the V^T ring shares), V(1) at the start of iteration 0.
+    // have landed and every wave has read its Q rows out of the area the V^T
+    // ring shares, V(1) at the start of iteration 0.
     f32x16 s_cur[2], s_nxt[2];
     if (n_tiles > 0) {
         load_k(key0(0), 0);
@@ -440,12 +432,12 @@ __device__ __forceinline__ void attention_tile(const AttnArgs& a, int32_t seq, i
         if (n_tiles > 1) load_v_into(key0(1), vreg1);
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // direct-to-LDS loads have landed
-    // the same wait as an instruction the compiler sees: the Q fragments'
+    // the same wait as an instruction the compiler sees: the prologue's
     // register loads are then known complete on every path into the loop (the
     // prologue's conditional QK leaves a path where they are not, and the loop
     // would otherwise wait for all loads before its first QK MFMA)
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-    if (q_stage != nullptr) {
+    {
         // the same per-lane addresses as the K fragments (row l32 of the wave's
         // rows, the same swizzle), moved to the wave's staging rows
         const int32_t qs = static_cast<int32_t>(q_stage - k_lds) + wave * kQStageWaveBytes;
@@ -457,7 +449,6 @@ __device__ __forceinline__ void attention_tile(const AttnArgs& a, int32_t seq, i
     if (n_tiles > 0) store_v(0);
 #pragma unroll
     for (int u = 0; u < kVLoads; ++u) vreg[u] = vreg1[u];
-    if (q_stage == nullptr) __syncthreads();
     hook.after_prologue();
     if (n_tiles > 0 && (!kCausal || key0(0) <= wave_last_q)) qk(s_cur, std::integral_constant<int, 0>{});
     __syncthreads();  // K(0) is overwritten by K(2) at the end of iteration 0
@@ -750,8 +741,8 @@ __device__ __forceinline__ void attention_queues(const AttnArgs& a, const QueueA
 // Distinct entry points so that profiles separate the two steps.
 __global__ __launch_bounds__(kThreads, 1) void chunk_attention_kernel(AttnArgs a) {
     __shared__ __attribute__((aligned(1024))) unsigned char k_lds[2 * kKTileBytes];
-    __shared__ __attribute__((aligned(16))) bf16_t vt_lds[2 * kVtTileElems];
-    attention_grid<false>(a, k_lds, vt_lds, nullptr);
+    __shared__ __attribute__((aligned(1024))) unsigned char vq_lds[kQStageBytes];  // V^T ring and Q staging
+    attention_grid<false>(a, k_lds, reinterpret_cast<bf16_t*>(vq_lds), vq_lds);
 }
 
 __global__ __launch_bounds__(kThreads, 1) void suffix_attention_kernel(AttnArgs a) {

@@ -40,6 +40,8 @@ EDGE = [
     W.Workload("one_query_long", (3000,), (1,), 3, 512, 64, 64, 1.0, 506),
     # requests with context but no new tokens between ones that have both
     W.Workload("zero_query_with_context", (300, 200, 0, 50), (0, 4, 3, 0), 2, 256, 16, 16, 1.0, 508),
+    # the most heads the library accepts (MLA_MAX_HEADS): row strides of 384 KB (K) and 256 KB (V)
+    W.Workload("max_heads", (100, 0, 37), (40, 3, 33), 1024, 128, 16, 16, 1.0, 509),
 ]
 
 

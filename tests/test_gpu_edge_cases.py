@@ -42,6 +42,10 @@ EDGE = [
     W.Workload("zero_query_with_context", (300, 200, 0, 50), (0, 4, 3, 0), 2, 256, 16, 16, 1.0, 508),
     # the most heads the library accepts (MLA_MAX_HEADS): row strides of 384 KB (K) and 256 KB (V)
     W.Workload("max_heads", (100, 0, 37), (40, 3, 33), 1024, 128, 16, 16, 1.0, 509),
+    # 500 requests in one chunk: the persistent attention launches' work tables do not fit
+    # their LDS copy, so chunk and suffix attention take the one-workgroup-per-tile form
+    W.Workload("many_requests", tuple(int(x) for x in np.random.default_rng(510).integers(1, 41, 500)),
+               tuple(int(x) for x in np.random.default_rng(511).integers(1, 4, 500)), 2, 16384, 4, 4, 1.0, 510),
 ]
 
 
